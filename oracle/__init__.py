@@ -1,0 +1,18 @@
+"""CPU oracle (test infrastructure): the slow reference used to check the GPU path.
+
+Only the tests, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package. The library never does.
+"""
+
+from .sigmoid_attention import (  # noqa: F401
+    backward,
+    backward_rows,
+    default_scalars,
+    forward,
+    forward_rows,
+    head_backward,
+    head_forward,
+    scores,
+    sigmoid,
+    tile_plan,
+)

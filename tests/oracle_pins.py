@@ -1,0 +1,407 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
+* a closed form;
+* the hand-worked example under tests/golden;
+* finite differences;
+* torch's autograd;
+* an invariant the pages state.
+
+The functions reach the oracle only through module attribute lookups
+(``osa.forward`` etc.). tests/test_oracle_mutations.py can therefore
+monkeypatch a planted mistake into the oracle and check that some pin fails.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import pathlib
+
+import numpy as np
+
+from oracle import sigmoid_attention as osa
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    assert np.allclose(a, b, rtol=rtol, atol=atol), f"{what}: max diff {np.max(np.abs(a - b))}"
+
+
+def _case(rng, Z, L, H, D, nq, nk, scale=1.0):
+    q = rng.standard_normal((Z, L, H, D)) * scale
+    k = rng.standard_normal((Z, L, H, D)) * scale
+    v = rng.standard_normal((Z, L, H, D))
+    do = rng.standard_normal((Z, L, H, D))
+    return q, k, v, do, np.array(nq), np.array(nk)
+
+
+# --------------------------------------------------------------------------- sigma
+def pin_sigmoid_closed_forms():
+    """sigma(0) = 1/2 and sigma(+-ln 3) = 3/4, 1/4. It saturates to exactly 0
+    or 1 without overflow. sigma(-x) = 1 - sigma(x)."""
+    l3 = math.log(3.0)
+    x = np.array([0.0, l3, -l3, 800.0, -800.0, 30.0, -30.0])
+    want = [0.5, 0.75, 0.25, 1.0, 0.0, 1.0 / (1.0 + math.exp(-30.0)), math.exp(-30.0) / (1.0 + math.exp(-30.0))]
+    _close(osa.sigmoid(x), want, rtol=1e-15, atol=0, what="sigma closed forms")
+    r = np.random.default_rng(1).standard_normal(1000) * 8
+    _close(osa.sigmoid(-r), 1.0 - osa.sigmoid(r), rtol=0, atol=2e-16, what="sigma symmetry")
+    assert np.all(np.diff(osa.sigmoid(np.linspace(-50, 50, 2001))) >= 0), "sigma not monotone"
+
+
+def pin_derivative_bound():
+    """sigma' = sigma (1 - sigma) <= 1/4. So every |dS_ij| <= |dP_ij| / 4,
+    including at huge scores (rainbus.top summary, 核心方法; paperlayer.ai §3)."""
+    rng = np.random.default_rng(2)
+    for scale in (1.0, 4.0, 16.0):
+        qv = rng.standard_normal((40, 8)) * scale
+        kv = rng.standard_normal((33, 8)) * scale
+        vv = rng.standard_normal((33, 8))
+        dov = rng.standard_normal((40, 8))
+        _, _, _, it = osa.head_backward(qv, kv, vv, dov, 0.35, -2.0, return_intermediates=True)
+        p = it["P"]
+        assert np.all(p * (1 - p) <= 0.25), "sigma' above 1/4"
+        assert np.all(np.abs(it["dS"]) <= np.abs(it["dP"]) / 4 + 1e-300), "|dS| above |dP|/4"
+        _close(it["S"], 0.35 * qv @ kv.T - 2.0, rtol=1e-13, atol=1e-13, what="scores")
+
+
+def pin_lipschitz_quarter():
+    """sigma is 1/4-Lipschitz in the scores: ||sigma(S1)-sigma(S2)||_F <= ||S1-S2||_F / 4
+    (paperlayer.ai summary, A.1.2)."""
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        s1 = rng.standard_normal((16, 16)) * rng.uniform(0.1, 20)
+        s2 = s1 + rng.standard_normal((16, 16)) * rng.uniform(1e-3, 5)
+        lhs = np.linalg.norm(osa.sigmoid(s1) - osa.sigmoid(s2))
+        assert lhs <= 0.25 * np.linalg.norm(s1 - s2) * (1 + 1e-12), "sigma not 1/4-Lipschitz"
+
+
+# --------------------------------------------------------------------------- closed forms
+def pin_q_zero_closed_form():
+    """With Q = 0 every score equals b. Then, for i < n_q and j < n_k:
+      O_i  = sigma(b) * sum_j V_j
+      dK_j = 0
+      dV_j = sigma(b) * sum_i dO_i
+      dQ_i = alpha sigma(b)(1 - sigma(b)) * sum_j (dO_i . V_j) K_j
+    Every padded row is 0."""
+    rng = np.random.default_rng(4)
+    Z, L, H, D = 2, 12, 2, 3
+    nq, nk = [12, 7], [9, 12]
+    alpha, bias = 0.7, -1.3
+    _, k, v, do, nq, nk = _case(rng, Z, L, H, D, nq, nk)
+    q = np.zeros_like(k)
+    sb = 1.0 / (1.0 + math.exp(1.3))
+    o_w = np.zeros((Z, L, H, D))
+    dq_w = np.zeros((Z, L, H, D))
+    dv_w = np.zeros((Z, L, H, D))
+    for z in range(Z):
+        for h in range(H):
+            a, b = nq[z], nk[z]
+            o_w[z, :a, h] = sb * v[z, :b, h].sum(0)
+            dv_w[z, :b, h] = sb * do[z, :a, h].sum(0)
+            for i in range(a):
+                acc = np.zeros(D)
+                for j in range(b):
+                    acc += float(do[z, i, h] @ v[z, j, h]) * k[z, j, h]
+                dq_w[z, i, h] = alpha * sb * (1 - sb) * acc
+    _close(osa.forward(q, k, v, nq, nk, alpha, bias), o_w, what="O with Q=0")
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    _close(dq, dq_w, what="dQ with Q=0")
+    _close(dk, np.zeros_like(dk), what="dK with Q=0")
+    _close(dv, dv_w, what="dV with Q=0")
+
+
+def pin_k_zero_closed_form():
+    """With K = 0 every score equals b. Then, for i < n_q and j < n_k:
+      O_i  = sigma(b) * sum_j V_j
+      dQ_i = 0
+      dK_j = alpha sigma(b)(1 - sigma(b)) * sum_i (dO_i . V_j) Q_i
+      dV_j = sigma(b) * sum_i dO_i"""
+    rng = np.random.default_rng(5)
+    Z, L, H, D = 2, 10, 1, 4
+    q, _, v, do, nq, nk = _case(rng, Z, L, H, D, [6, 10], [10, 3])
+    k = np.zeros_like(q)
+    alpha, bias = 0.5, 0.8
+    sb = 1.0 / (1.0 + math.exp(-0.8))
+    o_w = np.zeros((Z, L, H, D))
+    dk_w = np.zeros((Z, L, H, D))
+    dv_w = np.zeros((Z, L, H, D))
+    for z in range(Z):
+        a, b = nq[z], nk[z]
+        o_w[z, :a, 0] = sb * v[z, :b, 0].sum(0)
+        dv_w[z, :b, 0] = sb * do[z, :a, 0].sum(0)
+        for j in range(b):
+            acc = np.zeros(D)
+            for i in range(a):
+                acc += float(do[z, i, 0] @ v[z, j, 0]) * q[z, i, 0]
+            dk_w[z, j, 0] = alpha * sb * (1 - sb) * acc
+    _close(osa.forward(q, k, v, nq, nk, alpha, bias), o_w, what="O with K=0")
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    _close(dq, np.zeros_like(dq), what="dQ with K=0")
+    _close(dk, dk_w, what="dK with K=0")
+    _close(dv, dv_w, what="dV with K=0")
+
+
+def pin_single_key():
+    """With n_k = 1: O_i = sigma(alpha q_i . k_0 + b) v_0, element by element, using math.exp."""
+    rng = np.random.default_rng(6)
+    Z, L, H, D = 1, 5, 2, 3
+    q, k, v, _, nq, nk = _case(rng, Z, L, H, D, [4], [1])
+    alpha, bias = 0.9, -0.4
+    o = osa.forward(q, k, v, nq, nk, alpha, bias)
+    for h in range(H):
+        for i in range(L):
+            if i < 4:
+                s = alpha * sum(q[0, i, h, d] * k[0, 0, h, d] for d in range(D)) + bias
+                w = 1.0 / (1.0 + math.exp(-s))
+                want = [w * v[0, 0, h, d] for d in range(D)]
+            else:
+                want = [0.0] * D
+            _close(o[0, i, h], want, rtol=1e-13, atol=1e-15, what="O with n_k=1")
+
+
+def pin_worked_example():
+    """The hand-worked example in tests/golden/worked_example.json."""
+    g = json.loads((GOLDEN / "worked_example.json").read_text())
+    alpha = bias = math.log(3.0) / 2.0
+    q = np.array(g["q"], np.float64)[None, :, None, :]
+    k = np.array(g["k"], np.float64)[None, :, None, :]
+    v = np.array(g["v"], np.float64)[None, :, None, :]
+    do = np.array(g["do"], np.float64)[None, :, None, :]
+    for c in g["cases"]:
+        nq, nk = np.array([c["n_q"]]), np.array([c["n_k"]])
+        o = osa.forward(q, k, v, nq, nk, alpha, bias)
+        _close(o[0, :, 0], c["o"], rtol=1e-14, atol=1e-14, what=f"worked O ({c['name']})")
+        dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+        _close(dq[0, :, 0] / alpha, c["dq_over_alpha"], rtol=1e-14, atol=1e-14, what=f"worked dQ ({c['name']})")
+        _close(dk[0, :, 0] / alpha, c["dk_over_alpha"], rtol=1e-14, atol=1e-14, what=f"worked dK ({c['name']})")
+        _close(dv[0, :, 0], c["dv"], rtol=1e-14, atol=1e-14, what=f"worked dV ({c['name']})")
+
+
+# --------------------------------------------------------------------------- gradients
+def _loss(q, k, v, do, nq, nk, alpha, bias):
+    return float(np.sum(osa.forward(q, k, v, nq, nk, alpha, bias) * do))
+
+
+def pin_finite_differences():
+    """Central differences in fp64 of L = sum(O * dO) against the backward, entry by
+    entry. The shape is tiny: Z=2, H=1, L=8, D=4. The length pairs are (n_q, n_k) =
+    ([8,5],[8,5]) and ([6,3],[8,5]). Perturbing a padded entry must change nothing,
+    so its difference must be exactly 0."""
+    rng = np.random.default_rng(7)
+    alpha, bias = 0.6, -1.1
+    for nq_, nk_ in (([8, 5], [8, 5]), ([6, 3], [8, 5])):
+        q, k, v, do, nq, nk = _case(rng, 2, 8, 1, 4, nq_, nk_)
+        grads = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+        hstep = 1e-6
+        for t_idx, (t, g) in enumerate(zip((q, k, v), grads)):
+            n_valid = nq if t_idx == 0 else nk
+            for idx in np.ndindex(t.shape):
+                orig = t[idx]
+                t[idx] = orig + hstep
+                lp = _loss(q, k, v, do, nq, nk, alpha, bias)
+                t[idx] = orig - hstep
+                lm = _loss(q, k, v, do, nq, nk, alpha, bias)
+                t[idx] = orig
+                fd = (lp - lm) / (2 * hstep)
+                if idx[1] >= n_valid[idx[0]]:
+                    assert lp == lm, f"padded entry {idx} of tensor {t_idx} changed the loss"
+                    assert g[idx] == 0.0, f"padded gradient {idx} of tensor {t_idx} is {g[idx]}"
+                else:
+                    assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (
+                        f"FD mismatch tensor {t_idx} at {idx}: fd={fd} grad={g[idx]}")
+
+
+def pin_torch_autograd():
+    """The dense torch form of the pages' "PyTorch sigmoid attention" gives the same
+    results. It uses torch.sigmoid on the full padded score matrix, zeroes the
+    weights of padded keys, zeroes padded query rows, and differentiates with
+    autograd in float64 on the CPU."""
+    import torch
+
+    rng = np.random.default_rng(8)
+    Z, L, H, D = 3, 24, 2, 8
+    q, k, v, do, nq, nk = _case(rng, Z, L, H, D, [24, 13, 0], [17, 24, 9])
+    alpha, bias = 1.0 / math.sqrt(D), -math.log(L)
+    tq, tk, tv = (torch.tensor(t, dtype=torch.float64, requires_grad=True) for t in (q, k, v))
+    tdo = torch.tensor(do, dtype=torch.float64)
+    outs = []
+    for z in range(Z):
+        kmask = (torch.arange(L) < int(nk[z])).to(torch.float64)
+        qmask = (torch.arange(L) < int(nq[z])).to(torch.float64)
+        heads = []
+        for h in range(H):
+            s = alpha * tq[z, :, h, :] @ tk[z, :, h, :].T + bias
+            p = torch.sigmoid(s) * kmask[None, :]
+            heads.append((p @ tv[z, :, h, :]) * qmask[:, None])
+        outs.append(torch.stack(heads, dim=1))
+    o_t = torch.stack(outs, dim=0)
+    (o_t * tdo).sum().backward()
+    _close(osa.forward(q, k, v, nq, nk, alpha, bias), o_t.detach().numpy(), rtol=1e-11, atol=1e-13, what="O vs torch")
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    _close(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-13, what="dQ vs autograd")
+    _close(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-13, what="dK vs autograd")
+    _close(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-13, what="dV vs autograd")
+
+
+def pin_gradient_identities():
+    """Two exact identities of the chain rule:
+    sum <dQ, Q> = sum <dK, K> (both equal alpha * sum dS * QK^T), and
+    sum <dV, V> = sum <dO, O>."""
+    rng = np.random.default_rng(9)
+    q, k, v, do, nq, nk = _case(rng, 2, 20, 3, 5, [20, 11], [15, 20])
+    alpha, bias = 0.45, -2.0
+    o = osa.forward(q, k, v, nq, nk, alpha, bias)
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    do_valid = do.copy()
+    for z in range(2):
+        do_valid[z, nq[z]:] = 0.0
+    _close(np.sum(dq * q), np.sum(dk * k), rtol=1e-12, atol=1e-12, what="<dQ,Q> = <dK,K>")
+    _close(np.sum(dv * v), np.sum(do_valid * o), rtol=1e-12, atol=1e-12, what="<dV,V> = <dO,O>")
+
+
+# --------------------------------------------------------------------------- padding and symmetries
+def pin_padding_semantics():
+    """The padding semantics (rainbus.top summary, 方法步骤详情 step 2):
+    * every padded output row is exactly 0;
+    * valid outputs are bitwise unchanged when the padded inputs hold garbage or NaN;
+    * valid outputs are bitwise unchanged when L grows."""
+    rng = np.random.default_rng(10)
+    Z, L, H, D = 3, 16, 2, 4
+    q, k, v, do, nq, nk = _case(rng, Z, L, H, D, [16, 9, 0], [11, 16, 5])
+    alpha, bias = 0.5, -1.0
+    o = osa.forward(q, k, v, nq, nk, alpha, bias)
+    g = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    for z in range(Z):
+        assert np.all(o[z, nq[z]:] == 0.0), "padded O row not 0"
+        assert np.all(g[0][z, nq[z]:] == 0.0), "padded dQ row not 0"
+        assert np.all(g[1][z, nk[z]:] == 0.0) and np.all(g[2][z, nk[z]:] == 0.0), "padded dK/dV row not 0"
+    for fill in (np.nan, 1e30):
+        q2, k2, v2, do2 = (t.copy() for t in (q, k, v, do))
+        for z in range(Z):
+            q2[z, nq[z]:] = fill
+            do2[z, nq[z]:] = fill
+            k2[z, nk[z]:] = fill
+            v2[z, nk[z]:] = fill
+        assert np.array_equal(osa.forward(q2, k2, v2, nq, nk, alpha, bias), o), f"O depends on padding ({fill})"
+        g2 = osa.backward(q2, k2, v2, do2, nq, nk, alpha, bias)
+        for a, b in zip(g2, g):
+            assert np.array_equal(a, b), f"grads depend on padding ({fill})"
+    grow = lambda t: np.concatenate([t, rng.standard_normal((Z, 7, H, D))], axis=1)  # noqa: E731
+    o3 = osa.forward(grow(q), grow(k), grow(v), nq, nk, alpha, bias)
+    assert np.array_equal(o3[:, :L], o) and np.all(o3[:, L:] == 0), "O changes when L grows"
+    g3 = osa.backward(grow(q), grow(k), grow(v), grow(do), nq, nk, alpha, bias)
+    for a, b in zip(g3, g):
+        assert np.array_equal(a[:, :L], b) and np.all(a[:, L:] == 0), "grads change when L grows"
+
+
+def pin_symmetries():
+    """O is linear in V. Permuting the valid keys together with their values:
+    * leaves O and dQ unchanged (up to rounding);
+    * permutes the rows of dK and dV the same way.
+    Scaling alpha by c while scaling Q by 1/c leaves every output unchanged."""
+    rng = np.random.default_rng(11)
+    Z, L, H, D = 1, 14, 2, 5
+    q, k, v, do, nq, nk = _case(rng, Z, L, H, D, [12], [10])
+    alpha, bias = 0.3, -0.7
+    v2 = rng.standard_normal(v.shape)
+    o1 = osa.forward(q, k, v, nq, nk, alpha, bias)
+    o2 = osa.forward(q, k, v2, nq, nk, alpha, bias)
+    _close(osa.forward(q, k, 2.0 * v - 3.0 * v2, nq, nk, alpha, bias), 2.0 * o1 - 3.0 * o2, what="linearity in V")
+    perm = np.concatenate([rng.permutation(10), np.arange(10, L)])
+    kp, vp = k[:, perm], v[:, perm]
+    _close(osa.forward(q, kp, vp, nq, nk, alpha, bias), o1, what="key permutation O")
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    dqp, dkp, dvp = osa.backward(q, kp, vp, do, nq, nk, alpha, bias)
+    _close(dqp, dq, what="key permutation dQ")
+    _close(dkp, dk[:, perm], what="key permutation dK")
+    _close(dvp, dv[:, perm], what="key permutation dV")
+    dqs, dks, dvs = osa.backward(q / 4.0, k, v, do, nq, nk, alpha * 4.0, bias)
+    _close(osa.forward(q / 4.0, k, v, nq, nk, alpha * 4.0, bias), o1, what="alpha/Q scaling O")
+    _close(dqs, dq * 4.0, what="alpha/Q scaling dQ")
+    _close(dks, dk, what="alpha/Q scaling dK")
+
+
+def pin_large_scores():
+    """At very large scores (std of alpha q.k about 256, as in the stress shape):
+    * every output is finite;
+    * P saturates to exactly 0 and exactly 1;
+    * dS is exactly 0 wherever P does."""
+    rng = np.random.default_rng(12)
+    qv = rng.standard_normal((64, 16)) * 16 * 2
+    kv = rng.standard_normal((48, 16)) * 16 * 2
+    vv = rng.standard_normal((48, 16))
+    dov = rng.standard_normal((64, 16))
+    dq, dk, dv, it = osa.head_backward(qv, kv, vv, dov, 0.25, -math.log(8192), return_intermediates=True)
+    assert all(np.all(np.isfinite(t)) for t in (dq, dk, dv, it["P"], it["dS"])), "non-finite at large scores"
+    p = it["P"]
+    assert np.any(p == 0.0) and np.any(p == 1.0), "no saturation at |S| ~ 1e3"
+    assert np.all(it["dS"][(p == 0.0) | (p == 1.0)] == 0.0), "dS not 0 where P saturates"
+    assert np.all(np.isfinite(osa.head_forward(qv, kv, vv, 0.25, -math.log(8192))))
+
+
+def pin_row_sampling():
+    """forward_rows / backward_rows give the same rows as the full-tensor functions."""
+    rng = np.random.default_rng(13)
+    q, k, v, do, nq, nk = _case(rng, 2, 30, 2, 6, [30, 17], [22, 30])
+    alpha, bias = 0.4, -1.5
+    o = osa.forward(q, k, v, nq, nk, alpha, bias)
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    rows = np.array([0, 5, 16, 17, 21, 22, 29])
+    for z in range(2):
+        for h in range(2):
+            _close(osa.forward_rows(q, k, v, nq, nk, alpha, bias, z, h, rows), o[z, rows, h], what="forward_rows")
+            a, b, c = osa.backward_rows(q, k, v, do, nq, nk, alpha, bias, z, h, rows, rows)
+            _close(a, dq[z, rows, h], what="backward_rows dQ")
+            _close(b, dk[z, rows, h], what="backward_rows dK")
+            _close(c, dv[z, rows, h], what="backward_rows dV")
+
+
+def pin_tile_plan():
+    """The skip plan equals its closed form: query tile m pairs with ceil(n_k/BN)
+    key tiles when m*BM < n_q, and with none otherwise. The same holds for key
+    tiles with the roles swapped. Edge lengths are covered: 0, L, multiples of
+    the tile, and L not a multiple of the tile."""
+    rng = np.random.default_rng(14)
+    for L, bm, bn in ((256, 64, 64), (300, 128, 64), (1000, 64, 128), (17, 16, 32)):
+        n = np.concatenate([[0, L, bm, bn, 1, L - 1], rng.integers(0, L + 1, 6)])
+        nq, nk = n, np.roll(n, 3)
+        by_q, by_k = osa.tile_plan(nq, nk, L, bm, bn)
+        n_qt, n_kt = -(-L // bm), -(-L // bn)
+        for z in range(n.shape[0]):
+            for m in range(n_qt):
+                want = -(-int(nk[z]) // bn) if m * bm < nq[z] else 0
+                assert by_q[z, m] == want, f"tile plan q L={L} z={z} m={m}: {by_q[z, m]} != {want}"
+            for t in range(n_kt):
+                want = -(-int(nq[z]) // bm) if t * bn < nk[z] else 0
+                assert by_k[z, t] == want, f"tile plan k L={L} z={z} t={t}: {by_k[z, t]} != {want}"
+
+
+def pin_default_scalars():
+    """alpha = 1/sqrt(D) (gist.science §2.A) and b = -ln(L) (paperlayer.ai §3, n = L)."""
+    a, b = osa.default_scalars(64, 256)
+    assert a == 0.125 and abs(b + math.log(256)) < 1e-15
+
+
+ALL_PINS = [
+    pin_sigmoid_closed_forms,
+    pin_derivative_bound,
+    pin_lipschitz_quarter,
+    pin_q_zero_closed_form,
+    pin_k_zero_closed_form,
+    pin_single_key,
+    pin_worked_example,
+    pin_finite_differences,
+    pin_torch_autograd,
+    pin_gradient_identities,
+    pin_padding_semantics,
+    pin_symmetries,
+    pin_large_scores,
+    pin_row_sampling,
+    pin_tile_plan,
+    pin_default_scalars,
+]

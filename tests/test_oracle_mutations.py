@@ -1,0 +1,151 @@
+"""Plant plausible mistakes in the CPU oracle and check that some pin catches each.
+
+The mistakes are planted with monkeypatch on the CPU. Each one is a slip a
+person could make writing the oracle: a dropped term, a wrong sign, a wrong
+index, a transposed or swapped operand, an off-by-one in the mask. Every
+mutant must make at least one pin in tests/oracle_pins.py fail.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import sigmoid_attention as osa
+
+_orig_scores = osa.scores
+_orig_sigmoid = osa.sigmoid
+_orig_head_backward = osa.head_backward
+_orig_forward = osa.forward
+_orig_backward = osa.backward
+_orig_tile_plan = osa.tile_plan
+
+
+def _hb(variant):
+    """A head_backward with one planted mistake."""
+
+    def f(qv, kv, vv, dov, alpha, bias, return_intermediates=False):
+        qv, kv, vv, dov = (np.asarray(t, np.float64) for t in (qv, kv, vv, dov))
+        s = osa.scores(qv, kv, alpha, bias)
+        p = osa.sigmoid(s)
+        dp = dov @ (kv.T if variant == "dP uses K" else vv.T)
+        if variant == "dS drops (1-P)":
+            ds = p * dp
+        elif variant == "dS sign":
+            ds = -p * (1.0 - p) * dp
+        else:
+            ds = p * (1.0 - p) * dp
+        dq = (1.0 if variant == "dQ drops alpha" else alpha) * (ds @ (vv if variant == "dQ uses V" else kv))
+        dk = alpha * (ds.T @ (dov if variant == "dK uses dO" else qv))
+        if variant == "dV uses 1-P":
+            dv = (1.0 - p).T @ dov
+        elif variant == "dV uses Q":
+            dv = p.T @ qv
+        else:
+            dv = p.T @ dov
+        if variant == "dK scaled by alpha twice":
+            dk = alpha * dk
+        if return_intermediates:
+            return dq, dk, dv, {"S": s, "P": p, "dP": dp, "dS": ds}
+        return dq, dk, dv
+
+    return f
+
+
+def _forward_mask(variant):
+    """A full-batch forward that gets the padding wrong."""
+
+    def f(q, k, v, seqlens_q, seqlens_k, alpha, bias):
+        Z, L, H, D = np.asarray(q).shape
+        nq = np.asarray(seqlens_q).astype(int)
+        nk = np.asarray(seqlens_k).astype(int)
+        o = np.zeros((Z, L, H, D))
+        for z in range(Z):
+            a = L if variant == "padded queries not zeroed" else nq[z]
+            b = {"keys masked with n_q": nq[z], "one padded key read": min(L, nk[z] + 1)}.get(variant, nk[z])
+            for h in range(H):
+                o[z, :a, h] = osa.head_forward(q[z, :a, h], k[z, :b, h], v[z, :b, h], alpha, bias)
+        return o
+
+    return f
+
+
+def _backward_mask(variant):
+    def f(q, k, v, do, seqlens_q, seqlens_k, alpha, bias):
+        Z, L, H, D = np.asarray(q).shape
+        nq = np.asarray(seqlens_q).astype(int)
+        nk = np.asarray(seqlens_k).astype(int)
+        out = [np.zeros((Z, L, H, D)) for _ in range(3)]
+        for z in range(Z):
+            a, b = nq[z], nk[z]
+            bk = L if variant == "padded keys get gradients" else b
+            for h in range(H):
+                dq, _, _ = osa.head_backward(q[z, :a, h], k[z, :b, h], v[z, :b, h], do[z, :a, h], alpha, bias)
+                _, dk, dv = osa.head_backward(q[z, :a, h], k[z, :bk, h], v[z, :bk, h], do[z, :a, h], alpha, bias)
+                out[0][z, :a, h] = dq
+                out[1][z, :bk, h] = dk
+                out[2][z, :bk, h] = dv
+        return tuple(out)
+
+    return f
+
+
+def _tile_plan_off_by_one(seqlens_q, seqlens_k, L, block_q, block_k):
+    nq = np.asarray(seqlens_q).reshape(-1)
+    nk = np.asarray(seqlens_k).reshape(-1)
+    n_qt, n_kt = -(-L // block_q), -(-L // block_k)
+    by_q = np.zeros((nq.shape[0], n_qt), np.int64)
+    by_k = np.zeros((nq.shape[0], n_kt), np.int64)
+    for z in range(nq.shape[0]):
+        for m in range(n_qt):
+            for t in range(n_kt):
+                if m * block_q <= nq[z] and t * block_k <= nk[z]:  # "<=" instead of "<"
+                    by_q[z, m] += 1
+                    by_k[z, t] += 1
+    return by_q, by_k
+
+
+MUTANTS = {
+    "bias dropped": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(kv, float).T)),
+    "alpha dropped": ("scores", lambda qv, kv, a, b: (np.asarray(qv, float) @ np.asarray(kv, float).T) + b),
+    "bias sign": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(kv, float).T) - b),
+    "scores use Q Q^T": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(qv, float).T[:, : np.asarray(kv).shape[0]]) + b
+                         if np.asarray(qv).shape[0] >= np.asarray(kv).shape[0] else _orig_scores(qv, kv, a, b) * 1.01),
+    "sigma sign": ("sigmoid", lambda x: _orig_sigmoid(-np.asarray(x, float))),
+    "sigma of 2x (tanh slip)": ("sigmoid", lambda x: _orig_sigmoid(2.0 * np.asarray(x, float))),
+    "sigma without exp": ("sigmoid", lambda x: 1.0 / (1.0 + np.abs(np.asarray(x, float)))),
+    "dS drops (1-P)": ("head_backward", _hb("dS drops (1-P)")),
+    "dS sign": ("head_backward", _hb("dS sign")),
+    "dP uses K": ("head_backward", _hb("dP uses K")),
+    "dQ drops alpha": ("head_backward", _hb("dQ drops alpha")),
+    "dQ uses V": ("head_backward", _hb("dQ uses V")),
+    "dK uses dO": ("head_backward", _hb("dK uses dO")),
+    "dK scaled by alpha twice": ("head_backward", _hb("dK scaled by alpha twice")),
+    "dV uses 1-P": ("head_backward", _hb("dV uses 1-P")),
+    "dV uses Q": ("head_backward", _hb("dV uses Q")),
+    "padded queries not zeroed": ("forward", _forward_mask("padded queries not zeroed")),
+    "keys masked with n_q": ("forward", _forward_mask("keys masked with n_q")),
+    "one padded key read": ("forward", _forward_mask("one padded key read")),
+    "padded keys get gradients": ("backward", _backward_mask("padded keys get gradients")),
+    "tile plan off by one": ("tile_plan", _tile_plan_off_by_one),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(osa, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake '{name}'"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in oracle_pins.ALL_PINS:
+        pin()
+    assert math.isfinite(float(osa.sigmoid(np.array([0.0]))[0]))
