@@ -1,0 +1,134 @@
+/*
+ * sigattn.h: C ABI of the padding-aware, non-causal sigmoid attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation comes from the summaries of "Better Models, Faster Training:
+ * Sigmoid Attention for single-cell Foundation Models" (arXiv:2604.27124):
+ *   rainbus.top summary, section "方法步骤详情" (method steps), steps 1-5;
+ *   gist.science summary, section 2.A (the forward formula);
+ *   paperlayer.ai summary, section 3 (the bias b = -log n).
+ *
+ *   S = alpha * Q K^T + b,  P = sigma(S) (elementwise, no row normalisation),
+ *   O = P V.
+ *   Keys j >= n_k[z] get weight exactly 0. Rows i >= n_q[z] of O are written 0.
+ *   Backward, with P recomputed from Q and K:
+ *     dS = P (1 - P) (dO V^T),
+ *     dQ = alpha dS K,  dK = alpha dS^T Q,  dV = P^T dO.
+ *   dQ rows i >= n_q and dK, dV rows j >= n_k are written 0. dO rows i >= n_q
+ *   are never read.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are contiguous [Z, L, H, D] (batch, length, heads, head dim) with
+ *    D fastest. Q, K, V, dO, O, dQ, dK and dV all share this shape, and
+ *    queries and keys share L.
+ *  - dtype SIGATTN_BF16: bf16 storage. The two contractions run on bf16 MFMA
+ *    with fp32 accumulation. P and dS are rounded to bf16 (RNE) before they
+ *    enter an MFMA, and outputs are rounded to bf16 (RNE).
+ *    dtype SIGATTN_FP32: fp32 storage and fp32 arithmetic throughout (the
+ *    validation build).
+ *  - D must be 64 or 128.
+ *  - Lengths are int32[Z] arrays in DEVICE memory, read by the kernels, so the
+ *    host never synchronises. A value below 0 is treated as 0, and a value
+ *    above L as L. Padding is a suffix: positions [0, n) are valid.
+ *  - Padded input rows are never read, so their contents, NaN included, cannot
+ *    change any output.
+ *  - Every element of every output is written, padding included. The caller
+ *    need not clear outputs.
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    keeps no reference after the call returns and allocates no memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
+ *    null stream). Calls are reentrant and thread-safe. Overlapping calls that
+ *    write the same output race, as any two kernels would.
+ *  - A call with Z, L or H equal to 0 does nothing and returns SIGATTN_OK.
+ *  - Return value: SIGATTN_OK (0) or a negative sigattn_status. No entry point
+ *    throws, aborts or prints. sigattn_last_error() returns a message for the
+ *    calling thread's most recent failure.
+ *  - Optional tile counters (nullable device int32 buffers) record the
+ *    skip decisions: for each tile, how many tiles it was paired with.
+ */
+#ifndef SIGATTN_H
+#define SIGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SIGATTN_BF16 = 0, SIGATTN_FP32 = 1 } sigattn_dtype;
+
+typedef enum {
+  SIGATTN_OK = 0,
+  SIGATTN_EINVAL = -1,        /* null pointer, negative size, D not 64/128, misaligned
+                                 pointer, non-finite alpha/bias, grid too large */
+  SIGATTN_EUNSUPPORTED = -2,  /* unknown dtype */
+  SIGATTN_EHIP = -3,          /* a HIP launch failed; see sigattn_last_error() */
+  SIGATTN_EWORKSPACE = -4     /* workspace smaller than sigattn_workspace_size() */
+} sigattn_status;
+
+/* Which kernel a tile configuration or a counter refers to. */
+typedef enum { SIGATTN_KERNEL_FWD = 0, SIGATTN_KERNEL_DQ = 1, SIGATTN_KERNEL_DKDV = 2 } sigattn_kernel;
+
+/*
+ * Forward: o = sigma(alpha * q k^T + bias) v with padding (rainbus.top summary,
+ * 方法步骤详情 steps 1-3; gist.science summary 2.A).
+ *   q, k, v        [Z, L, H, D] inputs, read only on valid rows.
+ *   o              [Z, L, H, D] output. Rows >= n_q[z] are written 0.
+ *   seqlens_q/_k   int32[Z], device.
+ *   alpha, bias    score scale and bias. The pages use 1/sqrt(D) and -log(n).
+ *   workspace      device scratch of at least sigattn_workspace_size(FWD, ...)
+ *                  bytes. May be NULL when that size is 0.
+ *   tile_counts    NULL, or int32[Z * H * ceil(L / BQ)], where BQ is the forward's
+ *                  query tile from sigattn_tile_config. Entry (z, h, m) receives
+ *                  the number of key tiles that query tile m computed. It is 0
+ *                  when the tile lies wholly in padding and was skipped.
+ */
+int sigattn_fwd(const void* q, const void* k, const void* v, void* o,
+                const int32_t* seqlens_q, const int32_t* seqlens_k,
+                int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                void* workspace, size_t workspace_bytes,
+                int32_t* tile_counts, void* stream);
+
+/*
+ * Backward: dq, dk, dv from q, k, v and dout. P is recomputed, and neither O
+ * nor any saved statistic is needed (rainbus.top summary, 方法步骤详情 steps
+ * 4-5). Two independent kernels run on `stream`, one for dQ and one for dK/dV,
+ * so there are no atomics and the results are bitwise deterministic.
+ *   dout             [Z, L, H, D] upstream gradient. Rows >= n_q are not read.
+ *   dq, dk, dv       [Z, L, H, D] outputs. dq rows >= n_q and dk, dv rows >= n_k
+ *                    are written 0.
+ *   tile_counts_dq   NULL or int32[Z * H * ceil(L / BQ_dq)]: key tiles per query tile.
+ *   tile_counts_dkdv NULL or int32[Z * H * ceil(L / BK_dkdv)]: query tiles per key tile.
+ * All other arguments are as for sigattn_fwd.
+ */
+int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                void* dq, void* dk, void* dv,
+                const int32_t* seqlens_q, const int32_t* seqlens_k,
+                int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                void* workspace, size_t workspace_bytes,
+                int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
+
+/* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
+ * backward (any other value) needs for this shape. 0 means none. */
+size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype);
+
+/* The tile sizes a kernel uses, for reading the tile counters. block_q is the
+ * query tile and block_k the key tile. Returns SIGATTN_EINVAL for an unknown
+ * kernel, D or dtype. */
+int sigattn_tile_config(int kernel, int D, int dtype, int* block_q, int* block_k);
+
+/* A static description of a status code. */
+const char* sigattn_strerror(int status);
+
+/* The calling thread's most recent error message ("" if none). */
+const char* sigattn_last_error(void);
+
+/* Library version string. */
+const char* sigattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGATTN_H */

@@ -1,0 +1,71 @@
+"""Build the HIP library in-tree: padding_aware_sigmoid_amd/libsigattn.so (gfx950).
+
+The build is plain hipcc. Each source is compiled to an object in parallel,
+then they are linked into one shared library. Packed-FP32 VALU ops are
+disabled for all device code.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import pathlib
+import shutil
+import subprocess
+
+PKG = pathlib.Path(__file__).resolve().parent
+CSRC = PKG / "csrc"
+INCLUDE = PKG.parent / "include"
+LIB = PKG / "libsigattn.so"
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    """Compile every source for gfx950 and link libsigattn.so. Always rebuilds."""
+    cc = hipcc()
+    objdir = PKG / "_build"
+    objdir.mkdir(exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        obj = objdir / (pathlib.Path(src).stem + ".o")
+        jobs.append((obj, [cc, *COMMON_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        for out in ex.map(lambda j: _run(j[1]), jobs):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB.with_suffix(".so.tmp")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *[str(o) for o, _ in jobs]])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,171 @@
+// C ABI of the sigmoid-attention library: argument checks and dispatch.
+// Declarations and the contract live in include/sigattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sigattn.h"
+
+namespace sigattn {
+template <int D>
+hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, int, int,
+                           float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, int, int,
+                           float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, void*, void*, void*, const int32_t*,
+                           const int32_t*, int, int, int, float, float, float, int32_t*, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_bwd_fp32(const void*, const void*, const void*, const void*, void*, void*, void*, const int32_t*,
+                           const int32_t*, int, int, int, float, float, float, int32_t*, int32_t*, hipStream_t);
+}  // namespace sigattn
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, const char* detail = "") {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tile sizes per kernel, D and dtype. They must match the kernels' constants.
+bool tile_config(int kernel, int dtype, int* bq, int* bk) {
+  if (dtype == SIGATTN_BF16) {
+    switch (kernel) {
+      case SIGATTN_KERNEL_FWD: *bq = 128; *bk = 64; return true;
+      case SIGATTN_KERNEL_DQ: *bq = 128; *bk = 64; return true;
+      case SIGATTN_KERNEL_DKDV: *bq = 64; *bk = 128; return true;
+    }
+  } else if (dtype == SIGATTN_FP32) {
+    switch (kernel) {
+      case SIGATTN_KERNEL_FWD: *bq = 64; *bk = 32; return true;
+      case SIGATTN_KERNEL_DQ: *bq = 64; *bk = 32; return true;
+      case SIGATTN_KERNEL_DKDV: *bq = 32; *bk = 64; return true;
+    }
+  }
+  return false;
+}
+
+// Shared checks. Returns 0 when the call may proceed, 1 when there is nothing
+// to do (an empty batch), or a negative status.
+int check_common(int Z, int L, int H, int D, float alpha, float bias, int dtype, const int32_t* nq, const int32_t* nk) {
+  if (dtype != SIGATTN_BF16 && dtype != SIGATTN_FP32) return fail(SIGATTN_EUNSUPPORTED, "unsupported dtype%s");
+  if (Z < 0 || L < 0 || H < 0) return fail(SIGATTN_EINVAL, "Z, L and H must be >= 0%s");
+  if (D != 64 && D != 128) return fail(SIGATTN_EINVAL, "D must be 64 or 128%s");
+  if (!std::isfinite(alpha) || !std::isfinite(bias)) return fail(SIGATTN_EINVAL, "alpha and bias must be finite%s");
+  if (Z == 0 || L == 0 || H == 0) return 1;
+  if (nq == nullptr || nk == nullptr) return fail(SIGATTN_EINVAL, "seqlens_q and seqlens_k must not be NULL%s");
+  // Every kernel's grid is Z * H * ceil(L / 32) or fewer blocks, and element
+  // offsets are 64-bit. The grid must fit in 2^31 - 1 blocks.
+  const long long blocks = (long long)Z * H * ((L + 31) / 32);
+  if (blocks > 0x7fffffffLL) return fail(SIGATTN_EINVAL, "problem too large for one grid%s");
+  return 0;
+}
+
+int check_tensor(const void* p, const char* name) {
+  if (p == nullptr) return fail(SIGATTN_EINVAL, "tensor %s is NULL", name);
+  if (!aligned16(p)) return fail(SIGATTN_EINVAL, "tensor %s is not 16-byte aligned", name);
+  return 0;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SIGATTN_OK;
+  return fail(SIGATTN_EHIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+// log2(e), for sigma(x) = 1 / (1 + 2^(-x log2 e))
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int sigattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* seqlens_q,
+                const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                void* workspace, size_t workspace_bytes, int32_t* tile_counts, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(o, "o")))
+    return rc;
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_fwd_bf16<64>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st)
+                  : sigattn::launch_fwd_bf16<128>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st);
+  else
+    e = (D == 64) ? sigattn::launch_fwd_fp32<64>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st)
+                  : sigattn::launch_fwd_fp32<128>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st);
+  return hip_status(e);
+}
+
+int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
+                float bias, int dtype, void* workspace, size_t workspace_bytes, int32_t* tile_counts_dq,
+                int32_t* tile_counts_dkdv, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) ||
+      (rc = check_tensor(dv, "dv")))
+    return rc;
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_bwd_bf16<64>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
+                                                  c0, tile_counts_dq, tile_counts_dkdv, st)
+                  : sigattn::launch_bwd_bf16<128>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
+                                                   c0, tile_counts_dq, tile_counts_dkdv, st);
+  else
+    e = (D == 64) ? sigattn::launch_bwd_fp32<64>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
+                                                  c0, tile_counts_dq, tile_counts_dkdv, st)
+                  : sigattn::launch_bwd_fp32<128>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
+                                                   c0, tile_counts_dq, tile_counts_dkdv, st);
+  return hip_status(e);
+}
+
+size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype) {
+  (void)kernel;
+  (void)Z;
+  (void)L;
+  (void)H;
+  (void)D;
+  (void)dtype;
+  return 0;
+}
+
+int sigattn_tile_config(int kernel, int D, int dtype, int* block_q, int* block_k) {
+  if (block_q == nullptr || block_k == nullptr || (D != 64 && D != 128)) return SIGATTN_EINVAL;
+  return tile_config(kernel, dtype, block_q, block_k) ? SIGATTN_OK : SIGATTN_EINVAL;
+}
+
+const char* sigattn_strerror(int status) {
+  switch (status) {
+    case SIGATTN_OK: return "ok";
+    case SIGATTN_EINVAL: return "invalid argument";
+    case SIGATTN_EUNSUPPORTED: return "unsupported dtype";
+    case SIGATTN_EHIP: return "HIP error";
+    case SIGATTN_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* sigattn_last_error(void) { return g_last_error; }
+
+const char* sigattn_version(void) { return "sigattn-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

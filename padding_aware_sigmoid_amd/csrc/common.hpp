@@ -1,0 +1,79 @@
+// Device helpers shared by the sigmoid-attention kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sigattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 32x32x16 bf16 MFMA, fp32 accumulate (v_mfma_f32_32x32x16_bf16).
+// Lane l of a wave64 supplies:
+//   A: row l%32, k = 8*(l/32) + 0..7;
+//   B: column l%32, k = 8*(l/32) + 0..7.
+// Accumulator register r of lane l holds row (r/4)*8 + 4*(l/32) + r%4 and
+// column l%32. These layouts were checked on the device against a host product.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The row an accumulator register maps to (see mfma32).
+__device__ __forceinline__ constexpr int acc_row(int r, int half) { return (r >> 2) * 8 + 4 * half + (r & 3); }
+
+// Key (or query) order inside one 16-wide k-step when an accumulator is
+// reused as an A operand. k-slot 8*half + j of the operand holds
+// accumulator register 8*ks + j, i.e. row 16*ks + 8*(j/4) + 4*half + j%4.
+// The B operand fed with it must therefore use the same row order. The
+// transposed LDS read below does exactly that.
+
+// sigma(alpha * s + bias) for a raw dot product s, as 1 / (1 + 2^(c1*s + c0))
+// with c1 = -alpha*log2(e) and c0 = -bias*log2(e). It uses v_exp_f32 (2^x) and
+// v_rcp_f32. If 2^(...) overflows to +inf the result is exactly 0. If it
+// underflows to 0 the result is exactly 1. No NaN can arise from finite s.
+__device__ __forceinline__ float sigmoid_dot(float s, float c1, float c0) {
+  const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c1, c0));
+  return __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+// Transposed LDS read feeding the B operand of mfma32 from a row-major tile
+// T[row][col] (bf16, `ld` elements per row) whose rows are the contraction
+// index.
+//
+// ds_read_b64_tr_b16 works per group of 16 lanes (measured on gfx950). Lane i
+// of a group receives, for j = 0..3, element i%4 of the 8-byte chunk that lane
+// 4j + i/4 of the same group addresses.
+//
+// The result: lane l receives T[row0 + 8*part + 4*(l/32) + j][col0 + l%32] for
+// j = 0..3, where part 0 and part 1 are the two reads. That is the row order
+// described above for k-step rows row0..row0+15.
+__device__ __forceinline__ bf16x8 lds_read_b_tr(const __bf16* tile, int ld, int row0, int col0, int lane) {
+  const int g = lane >> 4;  // 16-lane group
+  const int s = lane & 15;
+  const int row = row0 + 4 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const __bf16* p0 = tile + row * ld + col;
+  const __bf16* p1 = p0 + 8 * ld;
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
+
+}  // namespace sigattn

@@ -1,0 +1,144 @@
+"""Torch-facing binding of the C ABI. It marshals tensors to pointers and sizes.
+
+The functions carry the C entry points' names. torch supplies device memory
+and the current HIP stream, and nothing else: every step of the attention runs
+in libsigattn.so's kernels. There is no CPU path. A missing library raises.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.BF16, torch.float32: _lib.FP32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"sigattn supports bfloat16 and float32 tensors, got {t.dtype}") from None
+
+
+def _check_tensors(ref: torch.Tensor, named: dict) -> None:
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [Z, L, H, D]")
+    if ref.device.type != "cuda":
+        raise ValueError("sigattn tensors must live on a HIP device")
+    for name, t in named.items():
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [Z, L, H, D]")
+
+
+def _lengths(n, Z: int, device) -> torch.Tensor:
+    if isinstance(n, torch.Tensor):
+        if n.dtype != torch.int32 or n.device != device or n.numel() != Z or not n.is_contiguous():
+            raise ValueError("sequence lengths must be a contiguous int32[Z] tensor on the tensors' device")
+        return n
+    t = torch.as_tensor(n, dtype=torch.int32).reshape(-1)
+    if t.numel() != Z:
+        raise ValueError(f"expected {Z} sequence lengths")
+    return t.to(device)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def default_alpha(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def default_bias(L: int) -> float:
+    return -math.log(L)
+
+
+def _workspace(kernel: int, q: torch.Tensor):
+    Z, L, H, D = q.shape
+    nbytes = _lib.workspace_size(kernel, Z, L, H, D, _dtype_code(q))
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device), nbytes
+
+
+def sigattn_fwd(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, out=None, tile_counts=None):
+    """O = sigma(alpha q k^T + bias) v with padding. Wraps the C entry point sigattn_fwd.
+
+    q, k, v: [Z, L, H, D] bf16 or fp32 on the device. seqlens_*: int32[Z].
+    alpha defaults to 1/sqrt(D) and bias to -log(L).
+    tile_counts, if given, is an int32 device tensor of Z*H*ceil(L/BQ) entries.
+    """
+    _check_tensors(q, {"k": k, "v": v})
+    Z, L, H, D = q.shape
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(L) if bias is None else float(bias)
+    nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check_tensors(q, {"out": o})
+    ws, wsb = _workspace(_lib.KERNEL_FWD, q)
+    lib = _lib.load()
+    _lib.check(lib.sigattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(), nk.data_ptr(),
+                               Z, L, H, D, alpha, bias, _dtype_code(q), None if ws is None else ws.data_ptr(), wsb,
+                               None if tile_counts is None else tile_counts.data_ptr(), _stream(q.device)))
+    return o
+
+
+def sigattn_bwd(q, k, v, dout, seqlens_q, seqlens_k, alpha=None, bias=None, dq=None, dk=None, dv=None,
+                tile_counts_dq=None, tile_counts_dkdv=None):
+    """(dq, dk, dv) of sigmoid attention. Wraps the C entry point sigattn_bwd."""
+    _check_tensors(q, {"k": k, "v": v, "dout": dout})
+    Z, L, H, D = q.shape
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(L) if bias is None else float(bias)
+    nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_tensors(q, {"dq": dq, "dk": dk, "dv": dv})
+    ws, wsb = _workspace(_lib.KERNEL_DQ, q)
+    lib = _lib.load()
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _lib.check(lib.sigattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                               dk.data_ptr(), dv.data_ptr(), nq.data_ptr(), nk.data_ptr(), Z, L, H, D, alpha, bias,
+                               _dtype_code(q), ptr(ws), wsb, ptr(tile_counts_dq), ptr(tile_counts_dkdv),
+                               _stream(q.device)))
+    return dq, dk, dv
+
+
+def sigattn_tile_config(kernel: int, D: int, dtype) -> tuple:
+    code = dtype if isinstance(dtype, int) else _DTYPES[dtype]
+    return _lib.tile_config(kernel, D, code)
+
+
+class SigmoidAttention(torch.autograd.Function):
+    """Autograd wrapper. The forward saves only its inputs, since the backward
+    recomputes P and needs neither O nor any row statistic."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        Z, L, H, D = q.shape
+        nq = _lengths(seqlens_q, Z, q.device)
+        nk = _lengths(seqlens_k, Z, q.device)
+        alpha = default_alpha(D) if alpha is None else float(alpha)
+        bias = default_bias(L) if bias is None else float(bias)
+        ctx.save_for_backward(q, k, v, nq, nk)
+        ctx.scalars = (alpha, bias)
+        return sigattn_fwd(q, k, v, nq, nk, alpha, bias)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        q, k, v, nq, nk = ctx.saved_tensors
+        alpha, bias = ctx.scalars
+        dq, dk, dv = sigattn_bwd(q, k, v, grad_out.contiguous(), nq, nk, alpha, bias)
+        return dq, dk, dv, None, None, None, None
+
+
+def sigmoid_attention(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None):
+    """Differentiable padding-aware sigmoid attention over [Z, L, H, D] tensors."""
+    return SigmoidAttention.apply(q, k, v, seqlens_q, seqlens_k, alpha, bias)

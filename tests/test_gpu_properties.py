@@ -1,0 +1,151 @@
+"""Properties of the GPU path that must hold exactly.
+
+* Skip decisions: the kernels' tile counters equal the oracle's tile plan.
+* Padded rows of every output are exactly 0.
+* Valid outputs are bitwise identical when the padding holds garbage, NaN or
+  Inf, and when L grows.
+* Two runs give bitwise identical results (no atomics).
+* Empty inputs are no-ops. Invalid arguments give error codes, not faults.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import device_inputs, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_bwd(q, k, v, do, nq, nk, alpha, bias, counters=False):
+    import padding_aware_sigmoid_amd as sa
+
+    Z, L, H, D = q.shape
+    tc = {}
+    if counters:
+        for name, kern, axis in (("fwd", sa.KERNEL_FWD, 0), ("dq", sa.KERNEL_DQ, 0), ("dkdv", sa.KERNEL_DKDV, 1)):
+            bq, bk = sa.sigattn_tile_config(kern, D, q.dtype)
+            ntiles = -(-L // (bq if axis == 0 else bk))
+            tc[name] = torch.full((Z * H * ntiles,), -7, dtype=torch.int32, device=q.device)
+    o = sa.sigattn_fwd(q, k, v, nq, nk, alpha, bias, tile_counts=tc.get("fwd"))
+    g = sa.sigattn_bwd(q, k, v, do, nq, nk, alpha, bias, tile_counts_dq=tc.get("dq"),
+                       tile_counts_dkdv=tc.get("dkdv"))
+    torch.cuda.synchronize()
+    return o, g, tc
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("fp32", 64)])
+def test_tile_counters_match_oracle_plan(dtype, D):
+    import padding_aware_sigmoid_amd as sa
+
+    Z, L, H = 5, 520, 2
+    n_q = np.array([520, 0, 1, 129, 384])
+    n_k = np.array([64, 520, 300, 0, 385])
+    note(f"tile counters dtype={dtype} D={D}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, dtype, seed=3)
+    args = device_inputs(q, k, v, do, n_q, n_k)
+    _, _, tc = _fwd_bwd(*args, 1 / math.sqrt(D), -math.log(L), counters=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for name, kern in (("fwd", sa.KERNEL_FWD), ("dq", sa.KERNEL_DQ), ("dkdv", sa.KERNEL_DKDV)):
+        bq, bk = sa.sigattn_tile_config(kern, D, tdt)
+        by_q, by_k = oracle.tile_plan(n_q, n_k, L, bq, bk)
+        want = by_q if name != "dkdv" else by_k
+        got = tc[name].cpu().numpy().reshape(Z, H, -1)
+        for h in range(H):
+            assert np.array_equal(got[:, h, :], want), f"{name}: skip decisions differ from the oracle plan"
+
+
+@pytest.mark.parametrize("fill", ["garbage", "nan", "inf"])
+def test_padding_contents_never_matter(fill):
+    Z, L, H, D = 3, 300, 2, 128
+    n = np.array([300, 77, 200])
+    note(f"padding fill={fill}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=4)
+    base = _fwd_bwd(*device_inputs(q, k, v, do, n, n), 1 / math.sqrt(D), -math.log(L))
+    val = {"garbage": 1e4, "nan": float("nan"), "inf": float("inf")}[fill]
+    q2, k2, v2, do2 = (t.clone() for t in (q, k, v, do))
+    for z in range(Z):
+        for t in (q2, k2, v2, do2):
+            t[z, int(n[z]):] = val
+    other = _fwd_bwd(*device_inputs(q2, k2, v2, do2, n, n), 1 / math.sqrt(D), -math.log(L))
+    assert torch.equal(base[0], other[0]), "O changed with the padding contents"
+    for a, b in zip(base[1], other[1]):
+        assert torch.equal(a, b), "a gradient changed with the padding contents"
+
+
+def test_growing_L_is_bitwise_invariant():
+    Z, L, H, D = 2, 256, 2, 64
+    n = np.array([256, 100])
+    note("growing L")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=6)
+    alpha, bias = 0.125, -math.log(256)
+    a = _fwd_bwd(*device_inputs(q, k, v, do, n, n), alpha, bias)
+    grow = lambda t: torch.cat([t, torch.randn(Z, 70, H, D).to(t.dtype)], dim=1)  # noqa: E731
+    b = _fwd_bwd(*device_inputs(grow(q), grow(k), grow(v), grow(do), n, n), alpha, bias)
+    assert torch.equal(a[0], b[0][:, :L]) and torch.all(b[0][:, L:] == 0)
+    for x, y in zip(a[1], b[1]):
+        assert torch.equal(x, y[:, :L]) and torch.all(y[:, L:] == 0)
+
+
+def test_bitwise_deterministic():
+    Z, L, H, D = 2, 400, 2, 128
+    n = np.array([400, 250])
+    note("determinism")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=7)
+    args = device_inputs(q, k, v, do, n, n)
+    a = _fwd_bwd(*args, 1 / math.sqrt(D), -math.log(L))
+    b = _fwd_bwd(*args, 1 / math.sqrt(D), -math.log(L))
+    assert torch.equal(a[0], b[0])
+    for x, y in zip(a[1], b[1]):
+        assert torch.equal(x, y)
+
+
+def test_lengths_are_clamped():
+    """Lengths below 0 act as 0, lengths above L act as L."""
+    Z, L, H, D = 2, 128, 1, 64
+    note("length clamping")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=8)
+    a = _fwd_bwd(*device_inputs(q, k, v, do, np.array([-5, 999]), np.array([L + 1, -1])), 0.125, -4.0)
+    b = _fwd_bwd(*device_inputs(q, k, v, do, np.array([0, L]), np.array([L, 0])), 0.125, -4.0)
+    assert torch.equal(a[0], b[0])
+    for x, y in zip(a[1], b[1]):
+        assert torch.equal(x, y)
+
+
+def test_empty_and_errors():
+    import padding_aware_sigmoid_amd as sa
+    from padding_aware_sigmoid_amd import _lib
+
+    lib = _lib.load()
+    note("empty inputs and error codes")
+    # An empty batch is a successful no-op.
+    e = torch.empty(0, 16, 2, 64, dtype=torch.bfloat16, device="cuda")
+    n0 = torch.empty(0, dtype=torch.int32, device="cuda")
+    o = sa.sigattn_fwd(e, e, e, n0, n0)
+    assert o.shape == e.shape
+    g = sa.sigattn_bwd(e, e, e, e, n0, n0)
+    assert all(t.shape == e.shape for t in g)
+    # Error codes: bad D, bad dtype, NULL tensor, misaligned pointer.
+    x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16, device="cuda")
+    n = torch.full((1,), 8, dtype=torch.int32, device="cuda")
+    p = x.data_ptr()
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 96, 1.0, 0.0, 0, None, 0, None, None) == -1
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 7, None, 0, None, None) == -2
+    assert lib.sigattn_fwd(None, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None, 0, None,
+                           None) == -1
+    assert lib.sigattn_fwd(p + 2, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None, 0, None,
+                           None) == -1
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, float("nan"), 0.0, 0, None, 0, None,
+                           None) == -1
+    torch.cuda.synchronize()
+    # Outputs are fully written even where the caller left garbage in them.
+    q, k, v, do = workloads.make_tensors(1, 96, 1, 64, "bf16", seed=9)
+    dq_, dk_, dv_, ddo, dnq, dnk = device_inputs(q, k, v, do, [50], [30])
+    out = torch.full_like(dq_, float("nan"))
+    sa.sigattn_fwd(dq_, dk_, dv_, dnq, dnk, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out)) and torch.all(out[:, 50:] == 0)
