@@ -1,0 +1,236 @@
+"""Benchmark: padding-aware sigmoid attention fwd + bwd on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nopad16k] [--no-cpu-baseline]
+
+Definitions:
+* A step is one pass of the whole hot path over one batch of resident
+  synthetic input: sigattn_fwd (one kernel), then sigattn_bwd_dkdv and
+  sigattn_bwd_dq (the two backward kernels), all on torch's current stream.
+* `value` is whole-step throughput in TFLOP/s. FLOPs are counted the pages'
+  way (valid tokens only; backward = 2.5x forward) and divided by host wall
+  time over exactly K steps, with a device synchronisation on both sides.
+* Each kernel is also timed with HIP events recorded on the stream it runs
+  on. Those times feed the per-kernel figures and the roofline of the
+  dominant kernel.
+* The line also carries the 25%-padding workload at the same shape per
+  sample. The pages report both no padding and 25% padding.
+
+One GPU only. --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
+KERNEL_SOURCES = ["padding_aware_sigmoid_amd/csrc/common.hpp", "padding_aware_sigmoid_amd/csrc/fwd.hip",
+                  "padding_aware_sigmoid_amd/csrc/bwd.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update((ROOT / p).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="nopad16k")
+    ap.add_argument("--pad-workload", default="pad25_16k", help="secondary workload reported in the same line ('' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def run_gpu(name, steps, warmup, seed=0):
+    import torch
+
+    import padding_aware_sigmoid_amd as sa
+    import workloads
+    from padding_aware_sigmoid_amd import accounting
+
+    inp = workloads.make_inputs(name, seed=seed)
+    w = inp["workload"]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    nq = torch.as_tensor(inp["seqlens_q"]).to(dev)
+    nk = torch.as_tensor(inp["seqlens_k"]).to(dev)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sa.sigattn_fwd(q, k, v, nq, nk, w.alpha, w.bias, out=o)
+        if ev is not None:
+            ev[1].record(stream)
+        sa.sigattn_bwd_dkdv(q, k, v, do, nq, nk, w.alpha, w.bias, dk=dk, dv=dv)
+        if ev is not None:
+            ev[2].record(stream)
+        sa.sigattn_bwd_dq(q, k, v, do, nq, nk, w.alpha, w.bias, dq=dq)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    t_dkdv = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    t_dq = sum(e[2].elapsed_time(e[3]) for e in events) / steps
+    fl = accounting.attention_flops(w.Z, w.L, w.H, w.D, inp["seqlens_q"], inp["seqlens_k"])
+    # Algorithmic contraction FLOPs of each kernel per valid score pair:
+    # fwd 4D (QK^T, PV), dK/dV 8D (S, dP, dV, dK), dQ 6D (S, dP, dQ).
+    pairs = float((inp["seqlens_q"].astype("int64") * inp["seqlens_k"].astype("int64")).sum()) * w.H
+    kern = {
+        "fwd": {"ms": t_fwd, "flop": 4.0 * w.D * pairs},
+        "dkdv": {"ms": t_dkdv, "flop": 8.0 * w.D * pairs},
+        "dq": {"ms": t_dq, "flop": 6.0 * w.D * pairs},
+    }
+    for kv in kern.values():
+        kv["tflops"] = kv["flop"] / (kv["ms"] * 1e-3) / 1e12
+        kv["frac_peak"] = kv["tflops"] / PEAK_BF16_TFLOPS
+    ms_step = elapsed / steps * 1e3
+    res = {
+        "workload": w,
+        "lengths": inp["seqlens_q"].tolist(),
+        "ms_per_step": ms_step,
+        "tflops_valid": fl["total_valid"] / (ms_step * 1e-3) / 1e12,
+        "tflops_padded": fl["total_padded"] / (ms_step * 1e-3) / 1e12,
+        "fwd_tflops_valid": fl["fwd_valid"] / (t_fwd * 1e-3) / 1e12,
+        "bwd_tflops_valid": fl["bwd_valid"] / ((t_dkdv + t_dq) * 1e-3) / 1e12,
+        "fwd_tflops_padded": fl["fwd_padded"] / (t_fwd * 1e-3) / 1e12,
+        "bwd_tflops_padded": fl["bwd_padded"] / ((t_dkdv + t_dq) * 1e-3) / 1e12,
+        "kernels": kern,
+        "flops": fl,
+    }
+    del q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, heads=2):
+    """The oracle, as it stands, on `heads` (z, h) heads of the workload at full length: fwd + bwd."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    w = workloads.WORKLOADS[name]
+    n = int(workloads.lengths(w, 0)[0])
+    q, k, v, do = workloads.make_tensors(1, w.L, heads, w.D, w.dtype, seed=0)
+    Q, K, V, DO = (t.float().numpy() for t in (q, k, v, do))
+    nn = np.array([n])
+    t0 = time.perf_counter()
+    oracle.forward(Q, K, V, nn, nn, w.alpha, w.bias)
+    oracle.backward(Q, K, V, DO, nn, nn, w.alpha, w.bias)
+    dt = time.perf_counter() - t0
+    flop = 3.5 * 4.0 * w.D * n * n * heads
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} (z,h) heads of {name} at full length (L={w.L}, n={n}, D={w.D}), fwd+bwd in NumPy "
+                      f"float64, {dt:.1f} s; FLOPs counted as for the GPU (3.5 x 4*D*n^2 per head)",
+            "seconds": round(dt, 2)}
+
+
+def traffic_for(kernel_name: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken
+    on the current kernel sources. Otherwise null."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except Exception:  # noqa: BLE001
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel_name)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path shards with no "
+              "communication, one (z, h) slice per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    import padding_aware_sigmoid_amd as sa
+
+    sa.load()
+    main_res = run_gpu(args.workload, args.steps, args.warmup)
+    pad_res = run_gpu(args.pad_workload, args.steps, args.warmup) if args.pad_workload not in ('', 'none') else None
+    w = main_res["workload"]
+    dom_name = max(main_res["kernels"], key=lambda k: main_res["kernels"][k]["ms"])
+    dom = main_res["kernels"][dom_name]
+    roofline = {"bound": "mfma", "kernel": f"{dom_name}_bf16<D={w.D}>", "achieved": round(dom["tflops"], 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom["tflops"] / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom_name, args.workload),
+                "launch_ms": round(dom["ms"], 4), "flop_per_launch": dom["flop"]}
+    line = {
+        "metric": "sigmoid-attn fwd+bwd TFLOPS, L=16K D=128 bf16 (valid-token FLOPs, bwd=2.5x fwd)",
+        "value": round(main_res["tflops_valid"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "Z": w.Z, "H": w.H, "L": w.L, "D": w.D, "alpha": w.alpha,
+                   "bias": round(w.bias, 6), "lengths": main_res["lengths"], "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_peak": round(main_res["tflops_valid"] / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(main_res["fwd_tflops_valid"], 2),
+        "bwd_tflops": round(main_res["bwd_tflops_valid"], 2),
+        "kernels": {k: {"ms": round(v["ms"], 4), "tflops": round(v["tflops"], 2), "frac_peak": round(v["frac_peak"], 4)}
+                    for k, v in main_res["kernels"].items()},
+        "roofline": roofline,
+    }
+    if pad_res is not None:
+        pw = pad_res["workload"]
+        line["pad25"] = {
+            "workload": pw.name, "Z": pw.Z, "H": pw.H, "L": pw.L, "D": pw.D, "lengths": pad_res["lengths"],
+            "ms_per_step": round(pad_res["ms_per_step"], 4),
+            "tflops_valid": round(pad_res["tflops_valid"], 2), "tflops_padded": round(pad_res["tflops_padded"], 2),
+            "fwd_tflops_valid": round(pad_res["fwd_tflops_valid"], 2),
+            "bwd_tflops_valid": round(pad_res["bwd_tflops_valid"], 2),
+            "tflops_loss_vs_nopad": round(1.0 - pad_res["tflops_valid"] / main_res["tflops_valid"], 4),
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,6 +109,22 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
                 void* workspace, size_t workspace_bytes,
                 int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
 
+/*
+ * The two halves of sigattn_bwd, for callers that want to place or time them
+ * separately (for example, on two streams). Each launches one kernel.
+ * sigattn_bwd_dkdv writes dk and dv. sigattn_bwd_dq writes dq. Arguments are as
+ * for sigattn_bwd. Together they compute exactly what sigattn_bwd computes,
+ * bit for bit.
+ */
+int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                     const int32_t* seqlens_q, const int32_t* seqlens_k,
+                     int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                     int32_t* tile_counts_dkdv, void* stream);
+int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                   const int32_t* seqlens_q, const int32_t* seqlens_k,
+                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts_dq, void* stream);
+
 /* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
  * backward (any other value) needs for this shape. 0 means none. */
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype);

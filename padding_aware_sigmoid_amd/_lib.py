@@ -20,6 +20,8 @@ KERNEL_FWD, KERNEL_DQ, KERNEL_DKDV = 0, 1, 2
 EXPORTED_SYMBOLS = (
     "sigattn_fwd",
     "sigattn_bwd",
+    "sigattn_bwd_dkdv",
+    "sigattn_bwd_dq",
     "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
@@ -50,6 +52,10 @@ def load():
     lib.sigattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp, vp,
                                 vp]
     lib.sigattn_bwd.restype = i32
+    lib.sigattn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
+    lib.sigattn_bwd_dkdv.restype = i32
+    lib.sigattn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
+    lib.sigattn_bwd_dq.restype = i32
     lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

@@ -15,12 +15,18 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, const i
 template <int D>
 hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, int, int,
                            float, float, int32_t*, hipStream_t);
-template <int D>
-hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, void*, void*, void*, const int32_t*,
-                           const int32_t*, int, int, int, float, float, float, int32_t*, int32_t*, hipStream_t);
-template <int D>
-hipError_t launch_bwd_fp32(const void*, const void*, const void*, const void*, void*, void*, void*, const int32_t*,
-                           const int32_t*, int, int, int, float, float, float, int32_t*, int32_t*, hipStream_t);
+#define SIGATTN_DECL_BWD(NAME)                                                                                   \
+  template <int D>                                                                                               \
+  hipError_t NAME(const void*, const void*, const void*, const void*, void*, void*, const int32_t*, const int32_t*, \
+                  int, int, int, float, float, float, int32_t*, hipStream_t);
+SIGATTN_DECL_BWD(launch_dkdv_bf16)
+SIGATTN_DECL_BWD(launch_dkdv_fp32)
+#define SIGATTN_DECL_DQ(NAME)                                                                                    \
+  template <int D>                                                                                               \
+  hipError_t NAME(const void*, const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, \
+                  int, int, float, float, float, int32_t*, hipStream_t);
+SIGATTN_DECL_DQ(launch_dq_bf16)
+SIGATTN_DECL_DQ(launch_dq_fp32)
 }  // namespace sigattn
 
 namespace {
@@ -84,6 +90,38 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace
 
+namespace {
+
+int launch_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, const int32_t* nq,
+                const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype, int32_t* tc,
+                hipStream_t st) {
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dkdv_bf16<128>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+  else
+    e = (D == 64) ? sigattn::launch_dkdv_fp32<64>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dkdv_fp32<128>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+  return hip_status(e);
+}
+
+int launch_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
+              const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype, int32_t* tc,
+              hipStream_t st) {
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_dq_bf16<64>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dq_bf16<128>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+  else
+    e = (D == 64) ? sigattn::launch_dq_fp32<64>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dq_fp32<128>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+  return hip_status(e);
+}
+
+}  // namespace
+
 extern "C" {
 
 int sigattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* seqlens_q,
@@ -122,20 +160,36 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, v
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) ||
       (rc = check_tensor(dv, "dv")))
     return rc;
-  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_bwd_bf16<64>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
-                                                  c0, tile_counts_dq, tile_counts_dkdv, st)
-                  : sigattn::launch_bwd_bf16<128>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
-                                                   c0, tile_counts_dq, tile_counts_dkdv, st);
-  else
-    e = (D == 64) ? sigattn::launch_bwd_fp32<64>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
-                                                  c0, tile_counts_dq, tile_counts_dkdv, st)
-                  : sigattn::launch_bwd_fp32<128>(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, Z, L, H, alpha, c1,
-                                                   c0, tile_counts_dq, tile_counts_dkdv, st);
-  return hip_status(e);
+  rc = launch_dkdv(q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv, st);
+  if (rc != SIGATTN_OK) return rc;
+  return launch_dq(q, k, v, dout, dq, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dq, st);
+}
+
+int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                     const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
+                     float bias, int dtype, int32_t* tile_counts_dkdv, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")))
+    return rc;
+  return launch_dkdv(q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                   const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
+                   float bias, int dtype, int32_t* tile_counts_dq, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dq, "dq")))
+    return rc;
+  return launch_dq(q, k, v, dout, dq, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dq,
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype) {

@@ -379,45 +379,61 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
 
 // --------------------------------------------------------------------------------- launchers
 template <int D>
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                           const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0,
-                           int32_t* tc_dq, int32_t* tc_dkdv, hipStream_t st) {
+hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                            const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1,
+                            float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
-  const long long b_kv = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
-  hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3((unsigned)b_kv), dim3(256), 0, st, (const __bf16*)q,
+  const long long blocks = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
+  hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L, H,
-                     alpha, c1, c0, tc_dkdv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long b_q = (long long)Z * H * ((L + C::BQ_DQ - 1) / C::BQ_DQ);
-  hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3((unsigned)b_q), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, nq, nk, L, H, alpha, c1, c0, tc_dq);
+                     alpha, c1, c0, tc);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_bwd_fp32(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                           const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0,
-                           int32_t* tc_dq, int32_t* tc_dkdv, hipStream_t st) {
-  const long long b_kv = (long long)Z * H * ((L + 63) / 64);
-  hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((unsigned)b_kv), dim3(64), 0, st, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)dout, (float*)dk, (float*)dv, nq, nk, L, H, alpha, c1, c0,
-                     tc_dkdv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long b_q = (long long)Z * H * ((L + 63) / 64);
-  hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3((unsigned)b_q), dim3(64), 0, st, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)dout, (float*)dq, nq, nk, L, H, alpha, c1, c0, tc_dq);
+hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
+                          const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0, int32_t* tc,
+                          hipStream_t st) {
+  using C = BwdCfg<D>;
+  const long long blocks = (long long)Z * H * ((L + C::BQ_DQ - 1) / C::BQ_DQ);
+  hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, nq, nk, L, H, alpha, c1, c0, tc);
   return hipGetLastError();
 }
 
-#define SIGATTN_INST_BWD(D)                                                                                       \
-  template hipError_t launch_bwd_bf16<D>(const void*, const void*, const void*, const void*, void*, void*, void*, \
-                                         const int32_t*, const int32_t*, int, int, int, float, float, float,      \
-                                         int32_t*, int32_t*, hipStream_t);                                        \
-  template hipError_t launch_bwd_fp32<D>(const void*, const void*, const void*, const void*, void*, void*, void*, \
-                                         const int32_t*, const int32_t*, int, int, int, float, float, float,      \
-                                         int32_t*, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_dkdv_fp32(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                            const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1,
+                            float c0, int32_t* tc, hipStream_t st) {
+  const long long blocks = (long long)Z * H * ((L + 63) / 64);
+  hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
+                     (const float*)v, (const float*)dout, (float*)dk, (float*)dv, nq, nk, L, H, alpha, c1, c0, tc);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_fp32(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
+                          const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0, int32_t* tc,
+                          hipStream_t st) {
+  const long long blocks = (long long)Z * H * ((L + 63) / 64);
+  hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
+                     (const float*)v, (const float*)dout, (float*)dq, nq, nk, L, H, alpha, c1, c0, tc);
+  return hipGetLastError();
+}
+
+#define SIGATTN_INST_BWD(D)                                                                                   \
+  template hipError_t launch_dkdv_bf16<D>(const void*, const void*, const void*, const void*, void*, void*,      \
+                                          const int32_t*, const int32_t*, int, int, int, float, float, float,  \
+                                          int32_t*, hipStream_t);                                              \
+  template hipError_t launch_dq_bf16<D>(const void*, const void*, const void*, const void*, void*,              \
+                                        const int32_t*, const int32_t*, int, int, int, float, float, float,    \
+                                        int32_t*, hipStream_t);                                                \
+  template hipError_t launch_dkdv_fp32<D>(const void*, const void*, const void*, const void*, void*, void*,      \
+                                          const int32_t*, const int32_t*, int, int, int, float, float, float,  \
+                                          int32_t*, hipStream_t);                                              \
+  template hipError_t launch_dq_fp32<D>(const void*, const void*, const void*, const void*, void*,              \
+                                        const int32_t*, const int32_t*, int, int, int, float, float, float,    \
+                                        int32_t*, hipStream_t);
 SIGATTN_INST_BWD(64)
 SIGATTN_INST_BWD(128)
 

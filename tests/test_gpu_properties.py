@@ -149,3 +149,19 @@ def test_empty_and_errors():
     sa.sigattn_fwd(dq_, dk_, dv_, dnq, dnk, out=out)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out)) and torch.all(out[:, 50:] == 0)
+
+
+def test_split_backward_entry_points_match():
+    """sigattn_bwd_dkdv + sigattn_bwd_dq give exactly what sigattn_bwd gives."""
+    import padding_aware_sigmoid_amd as sa
+
+    Z, L, H, D = 2, 300, 2, 128
+    n = np.array([300, 123])
+    note("split backward entry points")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=10)
+    dq_, dk_, dv_, ddo, dn, _ = device_inputs(q, k, v, do, n, n)
+    a = sa.sigattn_bwd(dq_, dk_, dv_, ddo, dn, dn)
+    gk, gv = sa.sigattn_bwd_dkdv(dq_, dk_, dv_, ddo, dn, dn)
+    gq = sa.sigattn_bwd_dq(dq_, dk_, dv_, ddo, dn, dn)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], gq) and torch.equal(a[1], gk) and torch.equal(a[2], gv)
