@@ -1,0 +1,85 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with status codes without launching anything."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "sigattn.h"
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sigattn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from padding_aware_sigmoid_amd import _lib
+
+    if not _lib.lib_path().exists():
+        pytest.skip("libsigattn.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_tile_config",
+              "sigattn_workspace_size", "sigattn_strerror", "sigattn_last_error", "sigattn_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from padding_aware_sigmoid_amd import _lib
+
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in sigattn.h but not exported"
+    assert set(_lib.EXPORTED_SYMBOLS) == set(_declared_functions())
+
+
+def test_argument_errors_need_no_gpu(lib):
+    null = None
+    # D not 64/128
+    assert lib.sigattn_fwd(null, null, null, null, null, null, 1, 8, 1, 96, 1.0, 0.0, 0, null, 0, null, null) == -1
+    assert b"D must be" in lib.sigattn_last_error()
+    # unknown dtype
+    assert lib.sigattn_fwd(null, null, null, null, null, null, 1, 8, 1, 64, 1.0, 0.0, 9, null, 0, null, null) == -2
+    # negative sizes
+    assert lib.sigattn_bwd(null, null, null, null, null, null, null, null, null, -1, 8, 1, 64, 1.0, 0.0, 0, null, 0,
+                           null, null, null) == -1
+    # non-finite scalars
+    assert lib.sigattn_bwd_dq(null, null, null, null, null, null, null, 1, 8, 1, 64, float("inf"), 0.0, 0, null,
+                              null) == -1
+    # NULL lengths with a non-empty batch
+    assert lib.sigattn_bwd_dkdv(null, null, null, null, null, null, null, null, 1, 8, 1, 64, 1.0, 0.0, 0, null,
+                                null) == -1
+    # NULL tensors (lengths non-NULL but never dereferenced on the host)
+    fake = ctypes.c_void_p(16)
+    assert lib.sigattn_fwd(null, null, null, null, fake, fake, 1, 8, 1, 64, 1.0, 0.0, 0, null, 0, null, null) == -1
+    assert b"is NULL" in lib.sigattn_last_error()
+    # misaligned tensor
+    assert lib.sigattn_fwd(ctypes.c_void_p(18), fake, fake, fake, fake, fake, 1, 8, 1, 64, 1.0, 0.0, 0, null, 0, null,
+                           null) == -1
+    assert b"aligned" in lib.sigattn_last_error()
+    # an empty batch is a no-op success, even with NULL pointers
+    assert lib.sigattn_fwd(null, null, null, null, null, null, 0, 8, 1, 64, 1.0, 0.0, 0, null, 0, null, null) == 0
+
+
+def test_strings_and_configs(lib):
+    from padding_aware_sigmoid_amd import _lib
+
+    assert lib.sigattn_strerror(0) == b"ok"
+    assert lib.sigattn_strerror(-3) == b"HIP error"
+    assert b"gfx950" in lib.sigattn_version()
+    for kern in (0, 1, 2):
+        for d in (64, 128):
+            for dt in (0, 1):
+                bq, bk = _lib.tile_config(kern, d, dt)
+                assert bq > 0 and bk > 0 and bq % 32 == 0 and bk % 32 == 0
+    with pytest.raises(_lib.SigattnError):
+        _lib.tile_config(5, 64, 0)
+    assert _lib.workspace_size(0, 1, 16384, 16, 128, 0) == 0
