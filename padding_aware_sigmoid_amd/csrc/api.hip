@@ -44,7 +44,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool tile_config(int kernel, int dtype, int* bq, int* bk) {
   if (dtype == SIGATTN_BF16) {
     switch (kernel) {
-      case SIGATTN_KERNEL_FWD: *bq = 128; *bk = 64; return true;
+      case SIGATTN_KERNEL_FWD: *bq = 256; *bk = 64; return true;
       case SIGATTN_KERNEL_DQ: *bq = 128; *bk = 64; return true;
       case SIGATTN_KERNEL_DKDV: *bq = 64; *bk = 128; return true;
     }

@@ -74,6 +74,39 @@ __device__ __forceinline__ bf16x8 lds_read_b_tr(const __bf16* tile, int ld, int 
   return r;
 }
 
+// Scheduling hint for one region of the key loop: N groups of one MFMA
+// followed by up to V VALU instructions. The MFMA pipe then runs beside the
+// sigma work instead of in separate bursts. (Mask bits: 0x008 MFMA,
+// 0x002 VALU.)
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
+// Keeps the computation of p in the current scheduling region. Without it the
+// optimiser sinks register-only arithmetic past the next barrier, towards its
+// first use, and the phase loses the VALU work meant to overlap its MFMAs. The
+// asm is empty: no instruction, no memory access.
+__device__ __forceinline__ void pin_before_barrier(bf16x8 (&p)[2][2]) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(p[a][b]));
+}
+
 __device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8). This remap gives each XCD a contiguous range of logical tile ids.
+// Neighbouring query tiles of one head then share an XCD's L2 and stream the
+// same K/V tiles at about the same time. It is a bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
+  return x * per + (x < rem ? x : rem) + i;
+}
 
 }  // namespace sigattn

@@ -6,8 +6,10 @@
 // section 2.A (forward formula).
 //
 // CDNA4 design (bf16):
-//  - One workgroup computes one query tile of BQ = 128 rows for one (z, h).
-//    It has 4 waves of 32 query rows each.
+//  - One workgroup computes one query tile of BQ = 256 rows for one (z, h).
+//    It has 4 waves (one per SIMD) of 64 query rows each. A wave's two 32-row
+//    blocks share every K and V operand read from LDS, which halves LDS
+//    traffic per MFMA compared with 32-row waves.
 //  - A query tile at or past n_q writes zeros and exits.
 //  - Only key tiles below n_k are visited, so wholly padded key tiles are
 //    skipped.
@@ -25,14 +27,98 @@ namespace sigattn {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BQ = 128;  // query rows per workgroup
-  static constexpr int BK = 64;   // keys per LDS tile
-  static constexpr int NWAVE = 4;
-  static constexpr int KS = D / 16;  // MFMA k-steps over the head dim
-  static constexpr int NB = D / 32;  // 32-wide column blocks of O
-  static constexpr int LD = D + 8;   // LDS row pitch (bf16), +16 B against bank conflicts
+  static constexpr int WQ = 64;           // query rows per wave (two 32-row MFMA blocks)
+  static constexpr int NWAVE = 4;         // one wave per SIMD
+  static constexpr int BQ = WQ * NWAVE;   // 256 query rows per workgroup
+  static constexpr int BK = 64;           // keys per LDS tile (two 32-key MFMA blocks)
+  static constexpr int NBUF = 3;          // LDS ring depth (tiles t-1, t, t+1 live at once)
+  static constexpr int KS = D / 16;       // MFMA k-steps over the head dim
+  static constexpr int NB = D / 32;       // 32-wide column blocks of O
+  static constexpr int LD = D + 8;        // LDS row pitch (bf16), +16 B against bank conflicts
+  static constexpr int TILE = BK * LD;    // elements of one K (or V) tile in LDS
+  static constexpr int CPR = D / 8;       // 16-byte chunks per row
+  static constexpr int CPT = BK * CPR / 256;  // chunks per thread per tile
 };
 
+// One K tile and one V tile held in registers between their global load and their LDS store.
+template <int D>
+struct KVStage {
+  bf16x8 k[FwdCfg<D>::CPT], v[FwdCfg<D>::CPT];
+};
+
+template <int D>
+__device__ __forceinline__ void kv_stage_load(KVStage<D>& st, const __bf16* __restrict__ Kb,
+                                              const __bf16* __restrict__ Vb, size_t rs, int k0, int nk, int tid) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    // Rows at or past n_k are never read. The load goes to row n_k - 1 (valid,
+    // since n_k >= 1 whenever a tile is loaded) and the value is replaced by zero.
+    const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, kr = k0 + r;
+    const bool ok = kr < nk;
+    const size_t off = (size_t)(ok ? kr : nk - 1) * rs + cc * 8;
+    const bf16x8 kv = *(const bf16x8*)(Kb + off), vv = *(const bf16x8*)(Vb + off);
+    st.k[i] = ok ? kv : zero_bf16x8();
+    st.v[i] = ok ? vv : zero_bf16x8();
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_stage_store(const KVStage<D>& st, __bf16* sK, __bf16* sV, int tid) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
+    *(bf16x8*)(sK + r * C::LD + cc * 8) = st.k[i];
+    *(bf16x8*)(sV + r * C::LD + cc * 8) = st.v[i];
+  }
+}
+
+// S^T for one 32-key block kb of a K tile and the wave's two 32-query blocks.
+template <int D>
+__device__ __forceinline__ void scores_t(f32x16 (&sacc)[2], const __bf16* sK, int kb, const bf16x8 (&qf)[2][FwdCfg<D>::KS],
+                                         int l32, int half) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) {
+    const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * C::LD + 16 * s + 8 * half);
+    sacc[0] = mfma32(a, qf[0][s], sacc[0]);
+    sacc[1] = mfma32(a, qf[1][s], sacc[1]);
+  }
+}
+
+// P = sigma(S) in registers, packed as the A operands (two k-steps of 16 keys) of P V.
+__device__ __forceinline__ void sigma_pack(bf16x8 (&p)[2][2], const f32x16 (&sacc)[2], float c1, float c0) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(sacc[qb][r], c1, c0);
+}
+
+// O += P V for one 32-key block kb of a V tile.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], const bf16x8 (&p)[2][2],
+                                              const __bf16* sV, int kb, int lane) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 b = lds_read_b_tr(sV, C::LD, kb * 32 + ks * 16, db * 32, lane);
+      oacc[0][db] = mfma32(p[0][ks], b, oacc[0][db]);
+      oacc[1][db] = mfma32(p[1][ks], b, oacc[1][db]);
+    }
+}
+
+// Forward. Each wave owns 64 query rows. The key loop is software-pipelined in
+// half-tiles (32 keys) so that the MFMAs of one half-tile run beside the sigma
+// of another. In key tile t:
+//   phase A: S(t, 2nd half) and O += P(t-1, 2nd half) V   ||   P(t, 1st half) = sigma(S)
+//   barrier; tile t+2 goes from registers to LDS; tile t+3 is fetched
+//   phase B: S(t+1, 1st half) and O += P(t, 1st half) V   ||   P(t, 2nd half) = sigma(S)
+// The LDS ring holds tiles t-1, t and t+1. There is one barrier per key tile.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -40,101 +126,111 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
                                                        const int32_t* __restrict__ seqlens_k, int L, int H, float c1,
                                                        float c0, int32_t* __restrict__ tile_counts) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[C::BK * C::LD];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[C::NBUF][C::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[C::NBUF][C::TILE];
 
   const int n_qt = (L + C::BQ - 1) / C::BQ;
-  int bid = blockIdx.x;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int m = bid % n_qt;
   bid /= n_qt;
   const int h = bid % H;
   const int z = bid / H;
   const int nq = clamp_len(seqlens_q[z], L);
   const int nk = clamp_len(seqlens_k[z], L);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const size_t rs = (size_t)H * D;  // elements between consecutive rows of one head
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const size_t rs = (size_t)H * D;
   const size_t base = ((size_t)z * L * H + h) * D;
-  const __bf16* Qb = Q + base;
   const __bf16* Kb = K + base;
   const __bf16* Vb = V + base;
   __bf16* Ob = O + base;
   const int q0 = m * C::BQ;
-  const int rows_here = min(C::BQ, L - q0);
 
   if (q0 >= nq) {  // wholly padded query tile: write zeros, skip all work
+    const int rows_here = min(C::BQ, L - q0);
     const bf16x8 zz = zero_bf16x8();
-    for (int c = tid; c < rows_here * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      *(bf16x8*)(Ob + (size_t)(q0 + r) * rs + cc * 8) = zz;
-    }
+    for (int c = tid; c < rows_here * C::CPR; c += 256)
+      *(bf16x8*)(Ob + (size_t)(q0 + c / C::CPR) * rs + (c % C::CPR) * 8) = zz;
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
     return;
   }
 
-  // Q fragment as the B operand of S^T = K Q^T: query row q0 + 32w + l%32, d = 16s + 8*half + 0..7.
-  const int qr = q0 + 32 * w + l32;
-  bf16x8 qf[C::KS];
+  // Q as the B operand of S^T = K Q^T: query row q0 + 64w + 32qb + l32, d = 16s + 8*half + 0..7.
+  bf16x8 qf[2][C::KS];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s)
-    qf[s] = (qr < nq) ? *(const bf16x8*)(Qb + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
-
-  f32x16 oacc[C::NB];
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = q0 + 64 * w + 32 * qb + l32;
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+    for (int s = 0; s < C::KS; ++s)
+      qf[qb][s] = (qr < nq) ? *(const bf16x8*)(Q + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
+  }
+  f32x16 oacc[2][C::NB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
 
   const int nkt = (nk + C::BK - 1) / C::BK;
-  for (int t = 0; t < nkt; ++t) {
-    const int k0 = t * C::BK;
-    for (int c = tid; c < C::BK * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      const int kr = k0 + r;
-      bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
-      if (kr < nk) {
-        kv = *(const bf16x8*)(Kb + (size_t)kr * rs + cc * 8);
-        vv = *(const bf16x8*)(Vb + (size_t)kr * rs + cc * 8);
-      }
-      *(bf16x8*)(sK + r * C::LD + cc * 8) = kv;
-      *(bf16x8*)(sV + r * C::LD + cc * 8) = vv;
+  if (nkt > 0) {
+    KVStage<D> st;
+    kv_stage_load<D>(st, Kb, Vb, rs, 0, nk, tid);
+    kv_stage_store<D>(st, sK[0], sV[0], tid);
+    if (nkt > 1) {
+      kv_stage_load<D>(st, Kb, Vb, rs, C::BK, nk, tid);
+      kv_stage_store<D>(st, sK[1], sV[1], tid);
     }
-    __syncthreads();
+    // Slot 2's V is read by the first phase A with P = 0 (there is no tile -1).
+    // It must hold finite values then, so it starts as zeros.
 #pragma unroll
-    for (int kb = 0; kb < C::BK / 32; ++kb) {
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * C::LD + 16 * s + 8 * half);
-        sacc = mfma32(a, qf[s], sacc);
-      }
-      bf16x8 p[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r >> 3][r & 7] = (__bf16)sigmoid_dot(sacc[r], c1, c0);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 b = lds_read_b_tr(sV, C::LD, kb * 32 + ks * 16, nb * 32, lane);
-          oacc[nb] = mfma32(p[ks], b, oacc[nb]);
-        }
+    for (int i = 0; i < C::CPT; ++i) {
+      const int c = tid + 256 * i;
+      *(bf16x8*)(sV[2] + (c / C::CPR) * C::LD + (c % C::CPR) * 8) = zero_bf16x8();
     }
+    if (nkt > 2) kv_stage_load<D>(st, Kb, Vb, rs, 2 * C::BK, nk, tid);
     __syncthreads();
+
+    f32x16 s_cur[2], s_nxt[2];
+    bf16x8 p0[2][2], p1[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) p1[qb][0] = p1[qb][1] = zero_bf16x8();
+    scores_t<D>(s_cur, sK[0], 0, qf, l32, half);
+    int bt = 0;  // LDS slot of tile t
+    for (int t = 0; t < nkt; ++t) {
+      const int bprev = (bt == 0) ? C::NBUF - 1 : bt - 1;
+      const int bnext = (bt == C::NBUF - 1) ? 0 : bt + 1;
+      // phase A: 32 MFMAs beside 32 sigmoids per lane
+      scores_t<D>(s_nxt, sK[bt], 1, qf, l32, half);
+      accumulate_pv<D>(oacc, p1, sV[bprev], 1, lane);
+      sigma_pack(p0, s_cur, c1, c0);
+      interleave_mfma_valu<4 * C::KS, 6>();
+      pin_before_barrier(p0);
+      __syncthreads();  // every wave is done with slot bprev
+      if (t + 2 < nkt) {
+        kv_stage_store<D>(st, sK[bprev], sV[bprev], tid);
+        if (t + 3 < nkt) kv_stage_load<D>(st, Kb, Vb, rs, (t + 3) * C::BK, nk, tid);
+      }
+      // phase B. When t + 1 == nkt the new S is computed from a stale slot and is never used.
+      scores_t<D>(s_cur, sK[bnext], 0, qf, l32, half);
+      accumulate_pv<D>(oacc, p0, sV[bt], 0, lane);
+      sigma_pack(p1, s_nxt, c1, c0);
+      interleave_mfma_valu<4 * C::KS, 6>();
+      bt = bnext;
+    }
+    // the last tile's second half
+    accumulate_pv<D>(oacc, p1, sV[bt == 0 ? C::NBUF - 1 : bt - 1], 1, lane);
   }
 
-  // Epilogue. Register r of oacc[nb] holds query row 32w + acc_row(r, half) and column nb*32 + l%32.
+  // Epilogue. Register r of oacc[qb][db] holds query row 64w + 32qb + acc_row(r, half), column 32db + l%32.
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = q0 + 32 * w + acc_row(r, half);
-      if (row < L) Ob[(size_t)row * rs + nb * 32 + l32] = (__bf16)(row < nq ? oacc[nb][r] : 0.0f);
-    }
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
+        if (row < L) Ob[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? oacc[qb][db][r] : 0.0f);
+      }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
 
