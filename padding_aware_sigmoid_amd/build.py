@@ -26,6 +26,9 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go to VGPRs where they fit. The sigma code then reads the
+    # scores without a v_accvgpr_read per value.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
 ]
 

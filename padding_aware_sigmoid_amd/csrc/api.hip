@@ -45,8 +45,8 @@ bool tile_config(int kernel, int dtype, int* bq, int* bk) {
   if (dtype == SIGATTN_BF16) {
     switch (kernel) {
       case SIGATTN_KERNEL_FWD: *bq = 256; *bk = 64; return true;
-      case SIGATTN_KERNEL_DQ: *bq = 128; *bk = 64; return true;
-      case SIGATTN_KERNEL_DKDV: *bq = 64; *bk = 128; return true;
+      case SIGATTN_KERNEL_DQ: *bq = 256; *bk = 64; return true;
+      case SIGATTN_KERNEL_DKDV: *bq = 64; *bk = 256; return true;
     }
   } else if (dtype == SIGATTN_FP32) {
     switch (kernel) {
@@ -71,6 +71,8 @@ int check_common(int Z, int L, int H, int D, float alpha, float bias, int dtype,
   // offsets are 64-bit. The grid must fit in 2^31 - 1 blocks.
   const long long blocks = (long long)Z * H * ((L + 31) / 32);
   if (blocks > 0x7fffffffLL) return fail(SIGATTN_EINVAL, "problem too large for one grid%s");
+  // Tiles reach LDS through buffer loads with 32-bit offsets below 256 rows.
+  if ((long long)H * D * 2 * 256 >= 0x80000000LL) return fail(SIGATTN_EINVAL, "H * D too large%s");
   return 0;
 }
 

@@ -20,21 +20,27 @@ namespace sigattn {
 
 template <int D>
 struct BwdCfg {
-  static constexpr int BQ_DQ = 128;   // dQ kernel: query rows per workgroup (4 waves x 32)
-  static constexpr int BK_DQ = 64;    // dQ kernel: keys per LDS tile
-  static constexpr int BK_KV = 128;   // dK/dV kernel: key rows per workgroup (4 waves x 32)
-  static constexpr int BQ_KV = 64;    // dK/dV kernel: queries per LDS tile
-  static constexpr int KS = D / 16;
-  static constexpr int NB = D / 32;
-  static constexpr int LD = D + 8;
+  static constexpr int W = 64;          // rows a wave owns: queries (dQ kernel) or keys (dK/dV kernel)
+  static constexpr int NWAVE = 4;       // one wave per SIMD
+  static constexpr int BQ_DQ = 256;     // dQ kernel: query rows per workgroup
+  static constexpr int BK_DQ = 64;      // dQ kernel: keys per LDS tile
+  static constexpr int BK_KV = 256;     // dK/dV kernel: key rows per workgroup
+  static constexpr int BQ_KV = 64;      // dK/dV kernel: queries per LDS tile
+  static constexpr int KS = D / 16;     // MFMA k-steps over the head dim
+  static constexpr int NB = D / 32;     // 32-wide column blocks of the gradients
+  static constexpr int TILE = 64 * D;   // elements of one 64-row LDS tile (swizzled, unpadded)
 };
 
 // ------------------------------------------------------------------------------------------ dQ
-// Wave w owns 32 query rows. It holds Q and dO as B operands, for:
+// Wave w owns 64 query rows (two 32-row blocks). It holds Q and dO as B
+// operands, for:
 //   S^T  = K Q^T   (A = K from LDS)
 //   dP^T = V dO^T  (A = V from LDS)
-// dS^T is built elementwise in registers and fed as the A operand of
+// dS^T = P (1 - P) dP^T is built in registers and fed as the A operand of
 // dQ += dS K. That product takes K from LDS through transposed reads.
+// Key tiles of 64 rows stream through a 2-slot LDS ring by DMA.
+// Per 32-key block, the next block's S^T / dP^T MFMAs run beside this block's
+// sigma and dS, and the previous block's dQ MFMAs run beside them too.
 template <int D>
 __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -42,10 +48,10 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
                                                       const int32_t* __restrict__ seqlens_k, int L, int H, float alpha,
                                                       float c1, float c0, int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[C::BK_DQ * C::LD];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[C::BK_DQ * C::LD];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][C::TILE];
   const int n_qt = (L + C::BQ_DQ - 1) / C::BQ_DQ;
-  int bid = blockIdx.x;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int m = bid % n_qt;
   bid /= n_qt;
   const int h = bid % H;
@@ -56,91 +62,139 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
   const size_t rs = (size_t)H * D;
   const size_t base = ((size_t)z * L * H + h) * D;
   const int q0 = m * C::BQ_DQ;
-  const int rows_here = min(C::BQ_DQ, L - q0);
   __bf16* dQb = dQ + base;
 
   if (q0 >= nq) {
+    const int rows_here = min(C::BQ_DQ, L - q0);
     const bf16x8 zz = zero_bf16x8();
-    for (int c = tid; c < rows_here * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      *(bf16x8*)(dQb + (size_t)(q0 + r) * rs + cc * 8) = zz;
-    }
+    for (int c = tid; c < rows_here * (D / 8); c += 256)
+      *(bf16x8*)(dQb + (size_t)(q0 + c / (D / 8)) * rs + (c % (D / 8)) * 8) = zz;
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
     return;
   }
 
-  const int qr = q0 + 32 * w + l32;
-  bf16x8 qf[C::KS], dof[C::KS];
+  bf16x8 qf[2][C::KS], dof[2][C::KS];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = q0 + 64 * w + 32 * qb + l32;
     const bool ok = qr < nq;
-    qf[s] = ok ? *(const bf16x8*)(Q + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
-    dof[s] = ok ? *(const bf16x8*)(dO + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      qf[qb][s] = ok ? *(const bf16x8*)(Q + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
+      dof[qb][s] = ok ? *(const bf16x8*)(dO + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
+    }
   }
-  f32x16 acc[C::NB];
+  f32x16 acc[2][C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
 
   const int nkt = (nk + C::BK_DQ - 1) / C::BK_DQ;
-  for (int t = 0; t < nkt; ++t) {
-    const int k0 = t * C::BK_DQ;
-    for (int c = tid; c < C::BK_DQ * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      const int kr = k0 + r;
-      bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
-      if (kr < nk) {
-        kv = *(const bf16x8*)(K + base + (size_t)kr * rs + cc * 8);
-        vv = *(const bf16x8*)(V + base + (size_t)kr * rs + cc * 8);
+  if (nkt > 0) {
+    const uint32_t row_bytes = (uint32_t)(rs * 2);
+    const __bf16* Kb = K + base;
+    const __bf16* Vb = V + base;
+    auto fetch = [&](int slot, int tile) {
+      const int k0 = tile * C::BK_DQ;
+      dma_tile<D, 64, 256>(sK[slot], Kb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+      dma_tile<D, 64, 256>(sV[slot], Vb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+    };
+    fetch(0, 0);
+    // dS of the previous 32-key block, waiting for its dQ MFMAs (zero before the first block).
+    bf16x8 ds_prev[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ds_prev[qb][0] = ds_prev[qb][1] = zero_bf16x8();
+    int slot_prev = 0;
+    for (int t = 0; t < nkt; ++t) {
+      const int slot = t & 1;
+      dma_wait();
+      __syncthreads();  // tile t is in LDS; every wave is done with tile t-1's dQ reads below
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T, dP^T for this block (32 MFMAs)
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          const bf16x8 ak = lds_nat<D>(sK[slot], kb * 32 + l32, 2 * s + half);
+          const bf16x8 av = lds_nat<D>(sV[slot], kb * 32 + l32, 2 * s + half);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sacc[qb] = mfma32(ak, qf[qb][s], sacc[qb]);
+            pacc[qb] = mfma32(av, dof[qb][s], pacc[qb]);
+          }
+        }
+        // the previous block's dQ (16 MFMAs), beside this block's sigma and dS
+        {
+          const __bf16* kt = (kb == 0) ? sK[slot_prev] : sK[slot];
+          const int kbp = (kb == 0) ? 1 : 0;
+#pragma unroll
+          for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const bf16x8 b = lds_tr<D>(kt, kbp * 32 + ks * 16, db * 32, lane);
+              acc[0][db] = mfma32(ds_prev[0][ks], b, acc[0][db]);
+              acc[1][db] = mfma32(ds_prev[1][ks], b, acc[1][db]);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = sigmoid_dot(sacc[qb][r], c1, c0);
+            ds_prev[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
+          }
+        interleave_mfma_valu<4 * C::KS + 2 * C::NB * 2, 6>();
+        if (kb == 0 && t + 1 < nkt) fetch(slot ^ 1, t + 1);  // slot ^ 1 held tile t-1, finished above
       }
-      *(bf16x8*)(sK + r * C::LD + cc * 8) = kv;
-      *(bf16x8*)(sV + r * C::LD + cc * 8) = vv;
+      slot_prev = slot;
     }
-    __syncthreads();
+    // dQ of the last block
 #pragma unroll
-    for (int kb = 0; kb < C::BK_DQ / 32; ++kb) {
-      f32x16 sacc, pacc;
+    for (int db = 0; db < C::NB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const int off = (kb * 32 + l32) * C::LD + 16 * s + 8 * half;
-        sacc = mfma32(*(const bf16x8*)(sK + off), qf[s], sacc);
-        pacc = mfma32(*(const bf16x8*)(sV + off), dof[s], pacc);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 b = lds_tr<D>(sK[slot_prev], 32 + ks * 16, db * 32, lane);
+        acc[0][db] = mfma32(ds_prev[0][ks], b, acc[0][db]);
+        acc[1][db] = mfma32(ds_prev[1][ks], b, acc[1][db]);
       }
-      bf16x8 ds[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = sigmoid_dot(sacc[r], c1, c0);
-        ds[r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[r]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          acc[nb] = mfma32(ds[ks], lds_read_b_tr(sK, C::LD, kb * 32 + ks * 16, nb * 32, lane), acc[nb]);
-    }
-    __syncthreads();
   }
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = q0 + 32 * w + acc_row(r, half);
-      if (row < L) dQb[(size_t)row * rs + nb * 32 + l32] = (__bf16)(row < nq ? alpha * acc[nb][r] : 0.0f);
-    }
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
+        if (row < L) dQb[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? alpha * acc[qb][db][r] : 0.0f);
+      }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
-// Wave w owns 32 key rows. It holds K and V as B operands, for:
+// Wave w owns 64 key rows (two 32-row blocks). It holds K and V as B operands, for:
 //   S  = Q K^T   (A = Q from LDS)
 //   dP = dO V^T  (A = dO from LDS)
 // P^T and dS^T come straight from those accumulators as A operands, for:
 //   dV += P^T dO   (B = dO through transposed LDS reads)
 //   dK += dS^T Q   (B = Q through transposed LDS reads)
-template <int D>
+// Query tiles of 64 rows stream through a 2-slot LDS ring by DMA.
+//
+// MODE selects what one launch computes:
+//   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
+//   KV_DK (S, dP, dK: 6*D) and KV_DV (S, dV: 4*D) split the work over two
+//   launches.
+// At D = 128 the K and V operands plus both accumulators do not fit one
+// wave's registers (the fused form spills), so D = 128 runs the split form.
+enum KvMode { KV_BOTH = 0, KV_DK = 1, KV_DV = 2 };
+
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         __bf16* __restrict__ dK, __bf16* __restrict__ dV,
@@ -149,10 +203,10 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
                                                         float alpha, float c1, float c0,
                                                         int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[C::BQ_KV * C::LD];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[C::BQ_KV * C::LD];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdO[2][C::TILE];
   const int n_kt = (L + C::BK_KV - 1) / C::BK_KV;
-  int bid = blockIdx.x;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int t = bid % n_kt;
   bid /= n_kt;
   const int h = bid % H;
@@ -163,89 +217,116 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   const size_t rs = (size_t)H * D;
   const size_t base = ((size_t)z * L * H + h) * D;
   const int k0 = t * C::BK_KV;
-  const int rows_here = min(C::BK_KV, L - k0);
   __bf16* dKb = dK + base;
   __bf16* dVb = dV + base;
 
+  constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   if (k0 >= nk) {
+    const int rows_here = min(C::BK_KV, L - k0);
     const bf16x8 zz = zero_bf16x8();
     for (int c = tid; c < rows_here * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      *(bf16x8*)(dKb + (size_t)(k0 + r) * rs + cc * 8) = zz;
-      *(bf16x8*)(dVb + (size_t)(k0 + r) * rs + cc * 8) = zz;
+      const size_t off = (size_t)(k0 + c / (D / 8)) * rs + (c % (D / 8)) * 8;
+      if (DO_DK) *(bf16x8*)(dKb + off) = zz;
+      if (DO_DV) *(bf16x8*)(dVb + off) = zz;
     }
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = 0;
     return;
   }
 
-  const int kr = k0 + 32 * w + l32;
-  bf16x8 kf[C::KS], vf[C::KS];
+  bf16x8 kf[2][C::KS], vf[2][C::KS];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) {
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kr = k0 + 64 * w + 32 * kb + l32;
     const bool ok = kr < nk;
-    kf[s] = ok ? *(const bf16x8*)(K + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
-    vf[s] = ok ? *(const bf16x8*)(V + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      kf[kb][s] = ok ? *(const bf16x8*)(K + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
+      if (DO_DK) vf[kb][s] = ok ? *(const bf16x8*)(V + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
+    }
   }
-  f32x16 dkacc[C::NB], dvacc[C::NB];
+  f32x16 dkacc[2][C::NB], dvacc[2][C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dkacc[nb][r] = dvacc[nb][r] = 0.0f;
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dkacc[kb][db][r] = dvacc[kb][db][r] = 0.0f;
 
   const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
-  for (int u = 0; u < nqt; ++u) {
-    const int qbase = u * C::BQ_KV;
-    for (int c = tid; c < C::BQ_KV * (D / 8); c += 256) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      const int qrow = qbase + r;
-      bf16x8 qv = zero_bf16x8(), dv = zero_bf16x8();
-      if (qrow < nq) {
-        qv = *(const bf16x8*)(Q + base + (size_t)qrow * rs + cc * 8);
-        dv = *(const bf16x8*)(dO + base + (size_t)qrow * rs + cc * 8);
-      }
-      *(bf16x8*)(sQ + r * C::LD + cc * 8) = qv;
-      *(bf16x8*)(sdO + r * C::LD + cc * 8) = dv;
-    }
-    __syncthreads();
+  if (nqt > 0) {
+    const uint32_t row_bytes = (uint32_t)(rs * 2);
+    const __bf16* Qb = Q + base;
+    const __bf16* dOb = dO + base;
+    auto fetch = [&](int slot, int tile) {
+      const int r0 = tile * C::BQ_KV;
+      dma_tile<D, 64, 256>(sQ[slot], Qb + (size_t)r0 * rs, row_bytes, nq - r0, tid);
+      dma_tile<D, 64, 256>(sdO[slot], dOb + (size_t)r0 * rs, row_bytes, nq - r0, tid);  // dV: B operand; dK: A of dP
+    };
+    fetch(0, 0);
+    for (int u = 0; u < nqt; ++u) {
+      const int slot = u & 1;
+      dma_wait();
+      __syncthreads();  // tile u is in LDS; every wave is done with tile u-1
+      if (u + 1 < nqt) fetch(slot ^ 1, u + 1);
 #pragma unroll
-    for (int qb = 0; qb < C::BQ_KV / 32; ++qb) {
-      f32x16 sacc, pacc;
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const int off = (qb * 32 + l32) * C::LD + 16 * s + 8 * half;
-        sacc = mfma32(*(const bf16x8*)(sQ + off), kf[s], sacc);
-        pacc = mfma32(*(const bf16x8*)(sdO + off), vf[s], pacc);
-      }
-      bf16x8 pt[2], dst[2];
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = pacc[kb][r] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = sigmoid_dot(sacc[r], c1, c0);
-        pt[r >> 3][r & 7] = (__bf16)p;
-        dst[r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[r]);
-      }
+        for (int s = 0; s < C::KS; ++s) {
+          const bf16x8 aq = lds_nat<D>(sQ[slot], qb * 32 + l32, 2 * s + half);
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(aq, kf[kb][s], sacc[kb]);
+          if (DO_DK) {
+            const bf16x8 ag = lds_nat<D>(sdO[slot], qb * 32 + l32, 2 * s + half);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvacc[nb] = mfma32(pt[ks], lds_read_b_tr(sdO, C::LD, qb * 32 + ks * 16, nb * 32, lane), dvacc[nb]);
-          dkacc[nb] = mfma32(dst[ks], lds_read_b_tr(sQ, C::LD, qb * 32 + ks * 16, nb * 32, lane), dkacc[nb]);
+            for (int kb = 0; kb < 2; ++kb) pacc[kb] = mfma32(ag, vf[kb][s], pacc[kb]);
+          }
         }
+        bf16x8 pt[2][2], dst[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = sigmoid_dot(sacc[kb][r], c1, c0);
+            if (DO_DV) pt[kb][r >> 3][r & 7] = (__bf16)p;
+            if (DO_DK) dst[kb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[kb][r]);
+          }
+#pragma unroll
+        for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (DO_DV) {
+              const bf16x8 bg = lds_tr<D>(sdO[slot], qb * 32 + ks * 16, db * 32, lane);
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) dvacc[kb][db] = mfma32(pt[kb][ks], bg, dvacc[kb][db]);
+            }
+            if (DO_DK) {
+              const bf16x8 bq = lds_tr<D>(sQ[slot], qb * 32 + ks * 16, db * 32, lane);
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) dkacc[kb][db] = mfma32(dst[kb][ks], bq, dkacc[kb][db]);
+            }
+          }
+        interleave_mfma_valu<(DO_DK ? 6 : 3) * C::KS, (DO_DK ? 8 : 6)>();
+      }
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = k0 + 32 * w + acc_row(r, half);
-      if (row < L) {
-        const bool ok = row < nk;
-        dKb[(size_t)row * rs + nb * 32 + l32] = (__bf16)(ok ? alpha * dkacc[nb][r] : 0.0f);
-        dVb[(size_t)row * rs + nb * 32 + l32] = (__bf16)(ok ? dvacc[nb][r] : 0.0f);
+    for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = k0 + 64 * w + 32 * kb + acc_row(r, half);
+        if (row < L) {
+          const bool ok = row < nk;
+          if (DO_DK) dKb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? alpha * dkacc[kb][db][r] : 0.0f);
+          if (DO_DV) dVb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? dvacc[kb][db][r] : 0.0f);
+        }
       }
-    }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = nqt;
 }
 
@@ -384,9 +465,21 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
                             float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
   const long long blocks = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
-  hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L, H,
-                     alpha, c1, c0, tc);
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_BOTH>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       H, alpha, c1, c0, tc);
+  } else {
+    // Both launches see the same lengths, so both write the same counters.
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DK>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       H, alpha, c1, c0, tc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DV>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       H, alpha, c1, c0, tc);
+  }
   return hipGetLastError();
 }
 

@@ -98,6 +98,111 @@ __device__ __forceinline__ void pin_before_barrier(bf16x8 (&p)[2][2]) {
     for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(p[a][b]));
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles: rows of D bf16, stored unpadded in 16-byte chunks with an XOR
+// swizzle. Physical chunk slot = logical chunk ^ swz(row). The swizzle makes
+// both operand reads conflict-free:
+//  - a natural read: 16 lanes, 16 consecutive rows, one chunk each;
+//  - a transposed read (ds_read_b64_tr_b16): 32 lanes, 4 consecutive rows,
+//    4 consecutive chunks.
+// It also lets whole tiles arrive by DMA (global -> LDS, 1 KB contiguous per
+// wave instruction), since no padding is needed.
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  // byte offset of logical chunk c of row r
+  __device__ static __forceinline__ int off(int r, int c) { return (r * CPR + (c ^ swz(r))) << 4; }
+};
+
+// Natural operand: 8 consecutive values of row r starting at logical chunk c.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_nat(const __bf16* tile, int r, int c) {
+  return *(const bf16x8*)((const char*)tile + Tile<D>::off(r, c));
+}
+
+// Transposed read feeding the B operand of mfma32 from a tile T[row][col]
+// whose rows are the contraction index.
+//
+// ds_read_b64_tr_b16 works per group of 16 lanes (measured on gfx950). Lane i
+// of a group receives, for j = 0..3, element i%4 of the 8-byte chunk that lane
+// 4j + i/4 of the same group addresses.
+//
+// The result: lane l receives T[row0 + 8*part + 4*(l/32) + j][col0 + l%32] for
+// j = 0..3, where part 0 and part 1 are the two reads. That is the k-step row
+// order described at mfma32.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr(const __bf16* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = row0 + 4 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const char* b = (const char*)tile;
+  const char* p0 = b + Tile<D>::off(row, col >> 3) + ((col & 7) << 1);
+  const char* p1 = b + Tile<D>::off(row + 8, col >> 3) + ((col & 7) << 1);
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS DMA (buffer_load_dwordx4 ... lds). Each lane fetches 16 bytes
+// at its byte offset into the buffer. The wave's 64 results land contiguously
+// at the LDS address of the instruction (lane l at +16*l). A lane whose offset
+// lies outside the buffer's range writes zeros (checked on the device).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned int* lds_u32_ptr;
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
+                                                           int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource over `bytes` bytes at p (raw, no stride), made wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  i32x4 v;
+  v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  v[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  v[3] = 0x00020000;  // dword format, as for every gfx9 raw buffer
+  return v;
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// DMA ROWS rows into a swizzled LDS tile. The tile's row i starts at byte
+// i * row_bytes after `rows` (row 0 of the tile in global memory). Rows at or
+// past n_valid are never read: their lanes take an out-of-range offset, so
+// the LDS receives zeros. The buffer resource covers only the valid rows, so
+// every offset stays below ROWS * row_bytes. Every wave of the workgroup takes
+// part. Call dma_wait() before the barrier that publishes the tile.
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid, int tid) {
+  constexpr int CPR = Tile<D>::CPR;
+  constexpr int SLOTS = ROWS * CPR;
+  static_assert(SLOTS % NTHREADS == 0, "tile must split evenly over the workgroup");
+  const int nv = n_valid < 0 ? 0 : (n_valid > ROWS ? ROWS : n_valid);
+  const i32x4 rsrc = make_rsrc(rows, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
+  const int lane = tid & 63, wbase = tid & ~63;
+#pragma unroll
+  for (int i = 0; i < SLOTS / NTHREADS; ++i) {
+    const int P0 = i * NTHREADS + wbase;  // wave-uniform first slot
+    const int P = P0 + lane;
+    const int r = P / CPR, cs = P % CPR;
+    const int c = cs ^ Tile<D>::swz(r);
+    const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
+    llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16),
+                                    16, (int)voff, 0, 0, 0);
+  }
+}
+
+// Wait until this wave's outstanding global loads (the DMAs included) are done.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
 __device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD

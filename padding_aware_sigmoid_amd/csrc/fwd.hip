@@ -13,10 +13,12 @@
 //  - A query tile at or past n_q writes zeros and exits.
 //  - Only key tiles below n_k are visited, so wholly padded key tiles are
 //    skipped.
-//  - K and V tiles are staged through LDS with coalesced 16-byte loads.
-//  - A padded key row is never read: its LDS row is filled with zeros. Its
-//    score is then b, and its weight is multiplied by V = 0. Its contribution
-//    is therefore exactly 0, whatever the padding holds.
+//  - K and V tiles reach LDS by DMA (16 bytes per lane, coalesced), into an
+//    XOR-swizzled layout.
+//  - A padded key row is never read: its lanes fetch out of range, so its LDS
+//    row holds zeros. Its score is then b, and its weight is multiplied by
+//    V = 0. Its contribution is therefore exactly 0, whatever the padding
+//    holds.
 //  - Scores are computed transposed, S^T = K Q^T, so the accumulator already
 //    has the layout of the A operand of P V. P never leaves registers.
 //  - V reaches the MFMA through ds_read_b64_tr_b16.
@@ -34,56 +36,19 @@ struct FwdCfg {
   static constexpr int NBUF = 3;          // LDS ring depth (tiles t-1, t, t+1 live at once)
   static constexpr int KS = D / 16;       // MFMA k-steps over the head dim
   static constexpr int NB = D / 32;       // 32-wide column blocks of O
-  static constexpr int LD = D + 8;        // LDS row pitch (bf16), +16 B against bank conflicts
-  static constexpr int TILE = BK * LD;    // elements of one K (or V) tile in LDS
-  static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static constexpr int CPT = BK * CPR / 256;  // chunks per thread per tile
+  static constexpr int TILE = BK * D;     // elements of one K (or V) tile in LDS (swizzled, unpadded)
 };
-
-// One K tile and one V tile held in registers between their global load and their LDS store.
-template <int D>
-struct KVStage {
-  bf16x8 k[FwdCfg<D>::CPT], v[FwdCfg<D>::CPT];
-};
-
-template <int D>
-__device__ __forceinline__ void kv_stage_load(KVStage<D>& st, const __bf16* __restrict__ Kb,
-                                              const __bf16* __restrict__ Vb, size_t rs, int k0, int nk, int tid) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    // Rows at or past n_k are never read. The load goes to row n_k - 1 (valid,
-    // since n_k >= 1 whenever a tile is loaded) and the value is replaced by zero.
-    const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, kr = k0 + r;
-    const bool ok = kr < nk;
-    const size_t off = (size_t)(ok ? kr : nk - 1) * rs + cc * 8;
-    const bf16x8 kv = *(const bf16x8*)(Kb + off), vv = *(const bf16x8*)(Vb + off);
-    st.k[i] = ok ? kv : zero_bf16x8();
-    st.v[i] = ok ? vv : zero_bf16x8();
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void kv_stage_store(const KVStage<D>& st, __bf16* sK, __bf16* sV, int tid) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
-    *(bf16x8*)(sK + r * C::LD + cc * 8) = st.k[i];
-    *(bf16x8*)(sV + r * C::LD + cc * 8) = st.v[i];
-  }
-}
 
 // S^T for one 32-key block kb of a K tile and the wave's two 32-query blocks.
 template <int D>
-__device__ __forceinline__ void scores_t(f32x16 (&sacc)[2], const __bf16* sK, int kb, const bf16x8 (&qf)[2][FwdCfg<D>::KS],
-                                         int l32, int half) {
+__device__ __forceinline__ void scores_t(f32x16 (&sacc)[2], const __bf16* sK, int kb,
+                                         const bf16x8 (&qf)[2][FwdCfg<D>::KS], int l32, int half) {
   using C = FwdCfg<D>;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = 0.0f;
 #pragma unroll
   for (int s = 0; s < C::KS; ++s) {
-    const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * C::LD + 16 * s + 8 * half);
+    const bf16x8 a = lds_nat<D>(sK, kb * 32 + l32, 2 * s + half);
     sacc[0] = mfma32(a, qf[0][s], sacc[0]);
     sacc[1] = mfma32(a, qf[1][s], sacc[1]);
   }
@@ -106,19 +71,77 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], 
   for (int db = 0; db < C::NB; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 b = lds_read_b_tr(sV, C::LD, kb * 32 + ks * 16, db * 32, lane);
+      const bf16x8 b = lds_tr<D>(sV, kb * 32 + ks * 16, db * 32, lane);
       oacc[0][db] = mfma32(p[0][ks], b, oacc[0][db]);
       oacc[1][db] = mfma32(p[1][ks], b, oacc[1][db]);
     }
+}
+
+// One pipeline phase of the forward for one wave, written as a fixed step
+// schedule. With one wave per SIMD, latency can only be hidden inside the
+// wave's own instruction stream.
+// The phase does three independent jobs:
+//   S_out = K(kb_s) Q^T   (KS steps of 2 MFMAs; A operand = a K row chunk)
+//   O += P_in V(kb_v)     (2*NB steps of 2 MFMAs; B operand = a V tr-read pair)
+//   P_out = sigma(S_in)   (32 values per lane, spread evenly over the steps)
+// The LDS operand of step j+2 is requested at step j (a 3-deep ring of
+// operand registers). An MFMA therefore never waits on a read issued just
+// before it, and the sigma work fills the MFMA pipe's busy cycles.
+template <int D>
+__device__ __forceinline__ void fwd_phase(f32x16 (&s_out)[2], const __bf16* sK, int kb_s,
+                                          f32x16 (&oacc)[2][FwdCfg<D>::NB], const bf16x8 (&p_in)[2][2],
+                                          const __bf16* sV, int kb_v, bf16x8 (&p_out)[2][2], const f32x16 (&s_in)[2],
+                                          const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0, int l32,
+                                          int half, int lane) {
+  using C = FwdCfg<D>;
+  constexpr int NSTEP = C::KS + 2 * C::NB;  // 16 at D = 128, 8 at D = 64
+  constexpr int EPS = 32 / NSTEP;           // sigma values per step
+  auto read = [&](int j) -> bf16x8 {
+    if (j < C::KS) return lds_nat<D>(sK, kb_s * 32 + l32, 2 * j + half);
+    const int i = j - C::KS;
+    return lds_tr<D>(sV, kb_v * 32 + (i & 1) * 16, (i >> 1) * 32, lane);
+  };
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s_out[0][r] = s_out[1][r] = 0.0f;
+  bf16x8 ops[3];
+  ops[0] = read(0);
+  ops[1] = read(1);
+#pragma unroll
+  for (int j = 0; j < NSTEP; ++j) {
+    if (j + 2 < NSTEP) ops[(j + 2) % 3] = read(j + 2);
+    const bf16x8 op = ops[j % 3];
+    if (j < C::KS) {
+      s_out[0] = mfma32(op, qf[0][j], s_out[0]);
+      s_out[1] = mfma32(op, qf[1][j], s_out[1]);
+    } else {
+      const int i = j - C::KS, db = i >> 1, ks = i & 1;
+      oacc[0][db] = mfma32(p_in[0][ks], op, oacc[0][db]);
+      oacc[1][db] = mfma32(p_in[1][ks], op, oacc[1][db]);
+    }
+#pragma unroll
+    for (int e = j * EPS; e < (j + 1) * EPS; ++e) {
+      const int qb = e >> 4, r = e & 15;
+      p_out[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_in[qb][r], c1, c0);
+    }
+    // keep the step's order: its LDS request, its two MFMAs, its sigma slice
+    if (j + 2 < C::KS)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    else if (j + 2 < NSTEP)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6 * EPS, 0);
+  }
 }
 
 // Forward. Each wave owns 64 query rows. The key loop is software-pipelined in
 // half-tiles (32 keys) so that the MFMAs of one half-tile run beside the sigma
 // of another. In key tile t:
 //   phase A: S(t, 2nd half) and O += P(t-1, 2nd half) V   ||   P(t, 1st half) = sigma(S)
-//   barrier; tile t+2 goes from registers to LDS; tile t+3 is fetched
+//   barrier; the DMA of tile t+2 into the slot tile t-1 held starts
 //   phase B: S(t+1, 1st half) and O += P(t, 1st half) V   ||   P(t, 2nd half) = sigma(S)
 // The LDS ring holds tiles t-1, t and t+1. There is one barrier per key tile.
+// K and V come straight from global memory into LDS by DMA, with padded key
+// rows replaced by zeros on the way.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -126,8 +149,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
                                                        const int32_t* __restrict__ seqlens_k, int L, int H, float c1,
                                                        float c0, int32_t* __restrict__ tile_counts) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[C::NBUF][C::TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[C::NBUF][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[C::NBUF][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[C::NBUF][C::TILE];
 
   const int n_qt = (L + C::BQ - 1) / C::BQ;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -140,16 +163,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)H * D;
   const size_t base = ((size_t)z * L * H + h) * D;
-  const __bf16* Kb = K + base;
-  const __bf16* Vb = V + base;
   __bf16* Ob = O + base;
   const int q0 = m * C::BQ;
 
   if (q0 >= nq) {  // wholly padded query tile: write zeros, skip all work
     const int rows_here = min(C::BQ, L - q0);
     const bf16x8 zz = zero_bf16x8();
-    for (int c = tid; c < rows_here * C::CPR; c += 256)
-      *(bf16x8*)(Ob + (size_t)(q0 + c / C::CPR) * rs + (c % C::CPR) * 8) = zz;
+    for (int c = tid; c < rows_here * (D / 8); c += 256)
+      *(bf16x8*)(Ob + (size_t)(q0 + c / (D / 8)) * rs + (c % (D / 8)) * 8) = zz;
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
     return;
   }
@@ -173,21 +194,20 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
 
   const int nkt = (nk + C::BK - 1) / C::BK;
   if (nkt > 0) {
-    KVStage<D> st;
-    kv_stage_load<D>(st, Kb, Vb, rs, 0, nk, tid);
-    kv_stage_store<D>(st, sK[0], sV[0], tid);
-    if (nkt > 1) {
-      kv_stage_load<D>(st, Kb, Vb, rs, C::BK, nk, tid);
-      kv_stage_store<D>(st, sK[1], sV[1], tid);
-    }
+    const uint32_t row_bytes = (uint32_t)(rs * 2);
+    const __bf16* Kb = K + base;
+    const __bf16* Vb = V + base;
+    auto fetch = [&](int slot, int tile) {  // DMA key tile `tile` into LDS slot `slot`
+      const int k0 = tile * C::BK;
+      dma_tile<D, C::BK, 256>(sK[slot], Kb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+      dma_tile<D, C::BK, 256>(sV[slot], Vb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+    };
+    fetch(0, 0);
+    if (nkt > 1) fetch(1, 1);
     // Slot 2's V is read by the first phase A with P = 0 (there is no tile -1).
     // It must hold finite values then, so it starts as zeros.
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + 256 * i;
-      *(bf16x8*)(sV[2] + (c / C::CPR) * C::LD + (c % C::CPR) * 8) = zero_bf16x8();
-    }
-    if (nkt > 2) kv_stage_load<D>(st, Kb, Vb, rs, 2 * C::BK, nk, tid);
+    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sV[2] + c * 8) = zero_bf16x8();
+    dma_wait();
     __syncthreads();
 
     f32x16 s_cur[2], s_nxt[2];
@@ -200,21 +220,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
       const int bprev = (bt == 0) ? C::NBUF - 1 : bt - 1;
       const int bnext = (bt == C::NBUF - 1) ? 0 : bt + 1;
       // phase A: 32 MFMAs beside 32 sigmoids per lane
-      scores_t<D>(s_nxt, sK[bt], 1, qf, l32, half);
-      accumulate_pv<D>(oacc, p1, sV[bprev], 1, lane);
-      sigma_pack(p0, s_cur, c1, c0);
-      interleave_mfma_valu<4 * C::KS, 6>();
+      fwd_phase<D>(s_nxt, sK[bt], 1, oacc, p1, sV[bprev], 1, p0, s_cur, qf, c1, c0, l32, half, lane);
       pin_before_barrier(p0);
-      __syncthreads();  // every wave is done with slot bprev
-      if (t + 2 < nkt) {
-        kv_stage_store<D>(st, sK[bprev], sV[bprev], tid);
-        if (t + 3 < nkt) kv_stage_load<D>(st, Kb, Vb, rs, (t + 3) * C::BK, nk, tid);
-      }
+      dma_wait();       // this wave's DMA of tile t+1 has landed
+      __syncthreads();  // ... everyone's has, and every wave is done with slot bprev
+      if (t + 2 < nkt) fetch(bprev, t + 2);
       // phase B. When t + 1 == nkt the new S is computed from a stale slot and is never used.
-      scores_t<D>(s_cur, sK[bnext], 0, qf, l32, half);
-      accumulate_pv<D>(oacc, p0, sV[bt], 0, lane);
-      sigma_pack(p1, s_nxt, c1, c0);
-      interleave_mfma_valu<4 * C::KS, 6>();
+      fwd_phase<D>(s_cur, sK[bnext], 0, oacc, p0, sV[bt], 0, p1, s_nxt, qf, c1, c0, l32, half, lane);
       bt = bnext;
     }
     // the last tile's second half
