@@ -38,9 +38,10 @@ struct BwdCfg {
 //   dP^T = V dO^T  (A = V from LDS)
 // dS^T = P (1 - P) dP^T is built in registers and fed as the A operand of
 // dQ += dS K. That product takes K from LDS through transposed reads.
-// Key tiles of 64 rows stream through a 2-slot LDS ring by DMA.
-// Per 32-key block, the next block's S^T / dP^T MFMAs run beside this block's
-// sigma and dS, and the previous block's dQ MFMAs run beside them too.
+// Key tiles of 64 rows stream through a 2-slot LDS ring by DMA. Per 32-key
+// block, the previous block's dQ MFMAs run beside this block's sigma and dS.
+// (A three-deep pipeline, like the dK/dV kernel's, needs more registers than
+// a wave has at D = 128. It spills, and it measured slower.)
 template <int D>
 __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -184,7 +185,12 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 // P^T and dS^T come straight from those accumulators as A operands, for:
 //   dV += P^T dO   (B = dO through transposed LDS reads)
 //   dK += dS^T Q   (B = Q through transposed LDS reads)
-// Query tiles of 64 rows stream through a 2-slot LDS ring by DMA.
+// The query axis runs in blocks of 32, pipelined three deep as in the dQ
+// kernel:
+//   A: S (and dP) of block i
+//   B: dV (and dK) += ... of block i-2
+//   V: P (and dS) of block i-1
+// Query tiles of 64 rows reach a 3-slot LDS ring by DMA.
 //
 // MODE selects what one launch computes:
 //   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
@@ -193,6 +199,83 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 // At D = 128 the K and V operands plus both accumulators do not fit one
 // wave's registers (the fused form spills), so D = 128 runs the split form.
 enum KvMode { KV_BOTH = 0, KV_DK = 1, KV_DV = 2 };
+
+template <int D, int MODE, bool DO_A, bool DO_B, bool DO_V>
+__device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, int qba, const __bf16* sQb,
+                                        const __bf16* sGb, int qbb, f32x16 (&sN)[2], f32x16 (&pN)[2],
+                                        f32x16 (&dkacc)[2][BwdCfg<D>::NB], f32x16 (&dvacc)[2][BwdCfg<D>::NB],
+                                        const bf16x8 (&ptB)[2][2], const bf16x8 (&dsB)[2][2], bf16x8 (&ptV)[2][2],
+                                        bf16x8 (&dsV)[2][2], const f32x16 (&sV)[2], const f32x16 (&pV)[2],
+                                        const bf16x8 (&kf)[2][BwdCfg<D>::KS], const bf16x8 (&vf)[2][BwdCfg<D>::KS],
+                                        float c1, float c0, int l32, int half, int lane) {
+  using C = BwdCfg<D>;
+  constexpr bool DK = MODE != KV_DV, DV = MODE != KV_DK;
+  constexpr int PA = DK ? 2 : 1;                // A operands per k-step: Q (and dO)
+  constexpr int PB = (DK ? 1 : 0) + (DV ? 1 : 0);  // B operands per (db, ks): dO tr (dV), Q tr (dK)
+  constexpr int NA = DO_A ? PA * C::KS : 0;
+  constexpr int NSTEP = NA + (DO_B ? PB * 2 * C::NB : 0);
+  constexpr int NV = DO_V ? 32 : 0;
+  // which job operand j belongs to: 0 = Q nat, 1 = dO nat, 2 = dO tr, 3 = Q tr
+  auto kind = [](int j) constexpr -> int {
+    if (j < NA) return (PA == 2 && (j & 1)) ? 1 : 0;
+    const int i = j - NA;
+    if (PB == 2) return (i & 1) ? 3 : 2;
+    return DV ? 2 : 3;
+  };
+  auto read = [&](auto jc) -> bf16x8 {
+    constexpr int j = decltype(jc)::value;
+    constexpr int k = kind(j);
+    if constexpr (k <= 1) {
+      return lds_nat<D>(k == 1 ? sGa : sQa, qba * 32 + l32, 2 * (j / PA) + half);
+    } else {
+      constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
+      return lds_tr<D>(k == 2 ? sGb : sQb, qbb * 32 + ks * 16, db * 32, lane);
+    }
+  };
+  if constexpr (DO_A) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sN[0][r] = sN[1][r] = 0.0f;
+      if constexpr (DK) pN[0][r] = pN[1][r] = 0.0f;
+    }
+  }
+  bf16x8 ops[3];
+  ops[0] = read(std::integral_constant<int, 0>{});
+  ops[1] = read(std::integral_constant<int, 1>{});
+  static_for<0, NSTEP>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int k = kind(j);
+    if constexpr (j + 2 < NSTEP) ops[(j + 2) % 3] = read(std::integral_constant<int, j + 2>{});
+    const bf16x8 op = ops[j % 3];
+    if constexpr (k == 0) {
+      constexpr int s = j / PA;
+      sN[0] = mfma32(op, kf[0][s], sN[0]);
+      sN[1] = mfma32(op, kf[1][s], sN[1]);
+    } else if constexpr (k == 1) {
+      constexpr int s = j / PA;
+      pN[0] = mfma32(op, vf[0][s], pN[0]);
+      pN[1] = mfma32(op, vf[1][s], pN[1]);
+    } else {
+      constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
+      if constexpr (k == 2) {
+        dvacc[0][db] = mfma32(ptB[0][ks], op, dvacc[0][db]);
+        dvacc[1][db] = mfma32(ptB[1][ks], op, dvacc[1][db]);
+      } else {
+        dkacc[0][db] = mfma32(dsB[0][ks], op, dkacc[0][db]);
+        dkacc[1][db] = mfma32(dsB[1][ks], op, dkacc[1][db]);
+      }
+    }
+    constexpr int e0 = j * NV / NSTEP, e1 = (j + 1) * NV / NSTEP;
+    static_for<e0, e1>([&](auto ec) {
+      constexpr int e = decltype(ec)::value, kb = e >> 4, r = e & 15;
+      const float p = sigmoid_dot(sV[kb][r], c1, c0);
+      if constexpr (DV) ptV[kb][r >> 3][r & 7] = (__bf16)p;
+      if constexpr (DK) dsV[kb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pV[kb][r]);
+    });
+    constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
+    sched_step<j, nds, 2, (e1 - e0) * (DK ? 7 : 5), kNoFence>();  // a hard fence makes the dK kernel spill
+  });
+}
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -203,8 +286,9 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
                                                         float alpha, float c1, float c0,
                                                         int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sdO[2][C::TILE];
+  constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[3][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdO[3][C::TILE];
   const int n_kt = (L + C::BK_KV - 1) / C::BK_KV;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int t = bid % n_kt;
@@ -220,7 +304,6 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   __bf16* dKb = dK + base;
   __bf16* dVb = dV + base;
 
-  constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   if (k0 >= nk) {
     const int rows_here = min(C::BK_KV, L - k0);
     const bf16x8 zz = zero_bf16x8();
@@ -260,59 +343,34 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
     auto fetch = [&](int slot, int tile) {
       const int r0 = tile * C::BQ_KV;
       dma_tile<D, 64, 256>(sQ[slot], Qb + (size_t)r0 * rs, row_bytes, nq - r0, tid);
-      dma_tile<D, 64, 256>(sdO[slot], dOb + (size_t)r0 * rs, row_bytes, nq - r0, tid);  // dV: B operand; dK: A of dP
+      dma_tile<D, 64, 256>(sdO[slot], dOb + (size_t)r0 * rs, row_bytes, nq - r0, tid);
     };
+    f32x16 sX[2], pX[2], sY[2], pY[2];
+    bf16x8 ptX[2][2], ptY[2][2], dsX[2][2], dsY[2][2];
     fetch(0, 0);
-    for (int u = 0; u < nqt; ++u) {
-      const int slot = u & 1;
+    dma_wait();
+    __syncthreads();
+    if (nqt > 1) fetch(1, 1);
+    kv_step<D, MODE, true, false, false>(sQ[0], sdO[0], 0, sQ[0], sdO[0], 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
+                                         dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
+    kv_step<D, MODE, true, false, true>(sQ[0], sdO[0], 1, sQ[0], sdO[0], 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX,
+                                        sX, pX, kf, vf, c1, c0, l32, half, lane);
+    int cur = 0, prev = 0;
+    for (int u = 1; u < nqt; ++u) {
+      prev = cur;
+      cur = (cur == 2) ? 0 : cur + 1;
       dma_wait();
-      __syncthreads();  // tile u is in LDS; every wave is done with tile u-1
-      if (u + 1 < nqt) fetch(slot ^ 1, u + 1);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc[2], pacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = pacc[kb][r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 aq = lds_nat<D>(sQ[slot], qb * 32 + l32, 2 * s + half);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(aq, kf[kb][s], sacc[kb]);
-          if (DO_DK) {
-            const bf16x8 ag = lds_nat<D>(sdO[slot], qb * 32 + l32, 2 * s + half);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) pacc[kb] = mfma32(ag, vf[kb][s], pacc[kb]);
-          }
-        }
-        bf16x8 pt[2][2], dst[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = sigmoid_dot(sacc[kb][r], c1, c0);
-            if (DO_DV) pt[kb][r >> 3][r & 7] = (__bf16)p;
-            if (DO_DK) dst[kb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[kb][r]);
-          }
-#pragma unroll
-        for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            if (DO_DV) {
-              const bf16x8 bg = lds_tr<D>(sdO[slot], qb * 32 + ks * 16, db * 32, lane);
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb) dvacc[kb][db] = mfma32(pt[kb][ks], bg, dvacc[kb][db]);
-            }
-            if (DO_DK) {
-              const bf16x8 bq = lds_tr<D>(sQ[slot], qb * 32 + ks * 16, db * 32, lane);
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb) dkacc[kb][db] = mfma32(dst[kb][ks], bq, dkacc[kb][db]);
-            }
-          }
-        interleave_mfma_valu<(DO_DK ? 6 : 3) * C::KS, (DO_DK ? 8 : 6)>();
-      }
+      __syncthreads();
+      if (u + 1 < nqt) fetch(cur == 2 ? 0 : cur + 1, u + 1);
+      kv_step<D, MODE, true, true, true>(sQ[cur], sdO[cur], 0, sQ[prev], sdO[prev], 0, sX, pX, dkacc, dvacc, ptX,
+                                         dsX, ptY, dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
+      kv_step<D, MODE, true, true, true>(sQ[cur], sdO[cur], 1, sQ[prev], sdO[prev], 1, sY, pY, dkacc, dvacc, ptY,
+                                         dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
     }
+    kv_step<D, MODE, false, true, true>(sQ[cur], sdO[cur], 0, sQ[cur], sdO[cur], 0, sX, pX, dkacc, dvacc, ptX, dsX,
+                                        ptY, dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
+    kv_step<D, MODE, false, true, false>(sQ[cur], sdO[cur], 0, sQ[cur], sdO[cur], 1, sY, pY, dkacc, dvacc, ptY, dsY,
+                                         ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sigattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -85,6 +87,43 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
   }
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = BEGIN .. END-1.
+// The index is a constant expression inside f, which the scheduling builtins
+// need.
+template <int I, int END, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < END) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, END>(f);
+  }
+}
+
+// One step of a software-pipelined schedule: NDS LDS reads, NMFMA MFMAs,
+// NVALU VALU instructions, in that order. Zero counts are skipped. After
+// every FENCE-th step a hard scheduling fence stops later instructions from
+// moving up and earlier ones from sinking. Without it the scheduler pairs
+// each MFMA with the LDS read right before it, and the read-ahead is lost.
+// The VALU work is split evenly behind each MFMA. An MFMA issued right after
+// another stalls the in-order wave until the matrix pipe frees, and the VALU
+// work placed between them fills those cycles.
+constexpr int kNoFence = 1 << 20;  // FENCE value that never fences
+
+template <int J, int NDS, int NMFMA, int NVALU, int FENCE = 2, bool SPLIT = true>
+__device__ __forceinline__ void sched_step() {
+  if constexpr (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  if constexpr (!SPLIT) {
+    if constexpr (NMFMA > 0) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+    if constexpr (NVALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+  } else static_for<0, NMFMA>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int v = (m + 1) * NVALU / NMFMA - m * NVALU / NMFMA;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);
+  });
+  if constexpr (NMFMA == 0 && NVALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+  if constexpr (J % FENCE == FENCE - 1) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Keeps the computation of p in the current scheduling region. Without it the

@@ -96,41 +96,38 @@ __device__ __forceinline__ void fwd_phase(f32x16 (&s_out)[2], const __bf16* sK, 
   using C = FwdCfg<D>;
   constexpr int NSTEP = C::KS + 2 * C::NB;  // 16 at D = 128, 8 at D = 64
   constexpr int EPS = 32 / NSTEP;           // sigma values per step
-  auto read = [&](int j) -> bf16x8 {
-    if (j < C::KS) return lds_nat<D>(sK, kb_s * 32 + l32, 2 * j + half);
-    const int i = j - C::KS;
-    return lds_tr<D>(sV, kb_v * 32 + (i & 1) * 16, (i >> 1) * 32, lane);
+  auto read = [&](auto jc) -> bf16x8 {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < C::KS) {
+      return lds_nat<D>(sK, kb_s * 32 + l32, 2 * j + half);
+    } else {
+      constexpr int i = j - C::KS;
+      return lds_tr<D>(sV, kb_v * 32 + (i & 1) * 16, (i >> 1) * 32, lane);
+    }
   };
 #pragma unroll
   for (int r = 0; r < 16; ++r) s_out[0][r] = s_out[1][r] = 0.0f;
   bf16x8 ops[3];
-  ops[0] = read(0);
-  ops[1] = read(1);
-#pragma unroll
-  for (int j = 0; j < NSTEP; ++j) {
-    if (j + 2 < NSTEP) ops[(j + 2) % 3] = read(j + 2);
+  ops[0] = read(std::integral_constant<int, 0>{});
+  ops[1] = read(std::integral_constant<int, 1>{});
+  static_for<0, NSTEP>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j + 2 < NSTEP) ops[(j + 2) % 3] = read(std::integral_constant<int, j + 2>{});
     const bf16x8 op = ops[j % 3];
-    if (j < C::KS) {
+    if constexpr (j < C::KS) {
       s_out[0] = mfma32(op, qf[0][j], s_out[0]);
       s_out[1] = mfma32(op, qf[1][j], s_out[1]);
     } else {
-      const int i = j - C::KS, db = i >> 1, ks = i & 1;
+      constexpr int i = j - C::KS, db = i >> 1, ks = i & 1;
       oacc[0][db] = mfma32(p_in[0][ks], op, oacc[0][db]);
       oacc[1][db] = mfma32(p_in[1][ks], op, oacc[1][db]);
     }
-#pragma unroll
-    for (int e = j * EPS; e < (j + 1) * EPS; ++e) {
-      const int qb = e >> 4, r = e & 15;
+    static_for<j * EPS, (j + 1) * EPS>([&](auto ec) {
+      constexpr int e = decltype(ec)::value, qb = e >> 4, r = e & 15;
       p_out[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_in[qb][r], c1, c0);
-    }
-    // keep the step's order: its LDS request, its two MFMAs, its sigma slice
-    if (j + 2 < C::KS)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    else if (j + 2 < NSTEP)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6 * EPS, 0);
-  }
+    });
+    sched_step<j, (j + 2 < NSTEP) ? ((j + 2 < C::KS) ? 1 : 2) : 0, 2, 5 * EPS, 2>();
+  });
 }
 
 // Forward. Each wave owns 64 query rows. The key loop is software-pipelined in
