@@ -46,17 +46,16 @@ template <int D>
 __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                       __bf16* __restrict__ dQ, const int32_t* __restrict__ seqlens_q,
-                                                      const int32_t* __restrict__ seqlens_k, int L, int H, float alpha,
-                                                      float c1, float c0, int32_t* __restrict__ tile_counts) {
+                                                      const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
+                                                      float alpha, float c1, float c0,
+                                                      int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 sK[2][C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV[2][C::TILE];
+  __shared__ int rank_lds[kMaxRankedSamples];
   const int n_qt = (L + C::BQ_DQ - 1) / C::BQ_DQ;
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int m = bid % n_qt;
-  bid /= n_qt;
-  const int h = bid % H;
-  const int z = bid / H;
+  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, L, seqlens_q, seqlens_k, rank_lds);
+  const int z = tcd.z, h = tcd.h, m = tcd.m;
   const int nq = clamp_len(seqlens_q[z], L);
   const int nk = clamp_len(seqlens_k[z], L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -282,19 +281,17 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                         const int32_t* __restrict__ seqlens_q,
-                                                        const int32_t* __restrict__ seqlens_k, int L, int H,
+                                                        const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
                                                         float alpha, float c1, float c0,
                                                         int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
   constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   __shared__ __attribute__((aligned(1024))) __bf16 sQ[3][C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sdO[3][C::TILE];
+  __shared__ int rank_lds[kMaxRankedSamples];
   const int n_kt = (L + C::BK_KV - 1) / C::BK_KV;
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = bid % n_kt;
-  bid /= n_kt;
-  const int h = bid % H;
-  const int z = bid / H;
+  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, L, seqlens_q, seqlens_k, rank_lds);
+  const int z = tcd.z, h = tcd.h, t = tcd.m;
   const int nq = clamp_len(seqlens_q[z], L);
   const int nk = clamp_len(seqlens_k[z], L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -525,17 +522,17 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
   const long long blocks = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
   if constexpr (D == 64) {
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_BOTH>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
                        H, alpha, c1, c0, tc);
   } else {
     // Both launches see the same lengths, so both write the same counters.
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DK>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
                        H, alpha, c1, c0, tc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DV>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, L,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
                        H, alpha, c1, c0, tc);
   }
   return hipGetLastError();
@@ -548,7 +545,7 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
   using C = BwdCfg<D>;
   const long long blocks = (long long)Z * H * ((L + C::BQ_DQ - 1) / C::BQ_DQ);
   hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, nq, nk, L, H, alpha, c1, c0, tc);
+                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, nq, nk, Z, L, H, alpha, c1, c0, tc);
   return hipGetLastError();
 }
 

@@ -126,6 +126,61 @@ __device__ __forceinline__ void sched_step() {
   if constexpr (J % FENCE == FENCE - 1) __builtin_amdgcn_sched_barrier(0);
 }
 
+__device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
+
+// ---------------------------------------------------------------------------
+// Tile scheduler. A grid covers every (sample z, head h, tile m). Blocks
+// whose tile lies wholly in padding exit at once, so the real work per
+// (z, h) is proportional to n_q[z] * n_k[z], which can vary widely across a
+// padded batch. The mapping block -> (z, h, m):
+//  - ranks samples by n_q * n_k, heaviest first (ties by index);
+//  - numbers the (sample, head) pairs in that order;
+//  - deals the pairs round-robin over the 8 XCDs (block b runs on XCD b % 8).
+// Each XCD then gets a similar share of heavy and light pairs and starts with
+// its heaviest (longest-processing-time first). All tiles of one pair stay on
+// one XCD, so that head's K/V (or Q/dO) stream through one L2.
+// With more than kMaxRankedSamples samples, or when the pair count is not a
+// multiple of 8, the mapping keeps the weight order but drops the XCD dealing.
+// rank_lds must hold kMaxRankedSamples ints. Every thread of the block calls
+// this, and it contains a barrier.
+constexpr int kMaxRankedSamples = 256;
+
+struct TileCoord {
+  int z, h, m;
+};
+
+__device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntiles, int L,
+                                                   const int32_t* __restrict__ seqlens_q,
+                                                   const int32_t* __restrict__ seqlens_k, int* rank_lds) {
+  const int P = Z * H;
+  int p, m;
+  if ((P & 7) == 0) {
+    const int x = b & 7, i = b >> 3;
+    p = x + 8 * (i / ntiles);
+    m = i % ntiles;
+  } else {
+    p = b / ntiles;
+    m = b % ntiles;
+  }
+  const int r = p / H, h = p - r * H;
+  int z = r;
+  if (Z <= kMaxRankedSamples) {
+    const int t = threadIdx.x;
+    if (t < Z) {
+      const long long wt = (long long)clamp_len(seqlens_q[t], L) * clamp_len(seqlens_k[t], L);
+      int rank = 0;
+      for (int u = 0; u < Z; ++u) {
+        const long long wu = (long long)clamp_len(seqlens_q[u], L) * clamp_len(seqlens_k[u], L);
+        rank += (wu > wt) || (wu == wt && u < t);
+      }
+      rank_lds[rank] = t;
+    }
+    __syncthreads();
+    z = rank_lds[r];
+  }
+  return {z, h, m};
+}
+
 // Keeps the computation of p in the current scheduling region. Without it the
 // optimiser sinks register-only arithmetic past the next barrier, towards its
 // first use, and the phase loses the VALU work meant to overlap its MFMAs. The
@@ -242,7 +297,6 @@ __device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* rows, uint3
 // Wait until this wave's outstanding global loads (the DMAs included) are done.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
-__device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8). This remap gives each XCD a contiguous range of logical tile ids.

@@ -143,18 +143,16 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                        const int32_t* __restrict__ seqlens_q,
-                                                       const int32_t* __restrict__ seqlens_k, int L, int H, float c1,
-                                                       float c0, int32_t* __restrict__ tile_counts) {
+                                                       const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
+                                                       float c1, float c0, int32_t* __restrict__ tile_counts) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 sK[C::NBUF][C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV[C::NBUF][C::TILE];
 
+  __shared__ int rank_lds[kMaxRankedSamples];
   const int n_qt = (L + C::BQ - 1) / C::BQ;
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int m = bid % n_qt;
-  bid /= n_qt;
-  const int h = bid % H;
-  const int z = bid / H;
+  const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, L, seqlens_q, seqlens_k, rank_lds);
+  const int z = tc.z, h = tc.h, m = tc.m;
   const int nq = clamp_len(seqlens_q[z], L);
   const int nk = clamp_len(seqlens_k[z], L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -308,7 +306,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   using C = FwdCfg<D>;
   const long long blocks = (long long)Z * H * ((L + C::BQ - 1) / C::BQ);
   hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, nq, nk, L, H, c1, c0, tc);
+                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, nq, nk, Z, L, H, c1, c0, tc);
   return hipGetLastError();
 }
 
