@@ -4,8 +4,10 @@
 
 Definitions:
 * A step is one pass of the whole hot path over one batch of resident
-  synthetic input: sigattn_fwd (one kernel), then sigattn_bwd_dkdv and
-  sigattn_bwd_dq (the two backward kernels), all on torch's current stream.
+  synthetic input: sigattn_fwd, then the backward (sigattn_bwd_dkdv at
+  D = 64; sigattn_bwd_dk and sigattn_bwd_dv at D = 128; then sigattn_bwd_dq),
+  one kernel per call, all on torch's current stream. This is exactly the
+  work of sigattn_fwd + sigattn_bwd.
 * `value` is whole-step throughput in TFLOP/s. FLOPs are counted the pages'
   way (valid tokens only; backward = 2.5x forward) and divided by host wall
   time over exactly K steps, with a device synchronisation on both sides.
@@ -21,9 +23,7 @@ One GPU only. --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
-import math
 import os
 import pathlib
 import sys
@@ -34,15 +34,6 @@ sys.path.insert(0, str(ROOT))
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
-KERNEL_SOURCES = ["padding_aware_sigmoid_amd/csrc/common.hpp", "padding_aware_sigmoid_amd/csrc/fwd.hip",
-                  "padding_aware_sigmoid_amd/csrc/bwd.hip"]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update((ROOT / p).read_bytes())
-    return h.hexdigest()[:16]
 
 
 def parse():
@@ -53,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="nopad16k")
     ap.add_argument("--pad-workload", default="pad25_16k", help="secondary workload reported in the same line ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many bytes twice (a plain device copy of "
+                         "known size that calibrates the rocprofv3 HBM byte counters); 0 skips it")
     return ap.parse_args()
 
 
@@ -72,43 +66,48 @@ def run_gpu(name, steps, warmup, seed=0):
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     stream = torch.cuda.current_stream(dev)
 
+    # The kernels of one step, in launch order, with each kernel's algorithmic
+    # contraction FLOPs per valid score pair: fwd 4D (QK^T, PV); dQ 6D (S, dP,
+    # dQ); dK/dV 8D (S, dP, dV, dK) when fused (D = 64), else dK 6D (S, dP, dK)
+    # and dV 4D (S, dV) as two launches (D = 128).
+    a, b = w.alpha, w.bias
+    launches = [("fwd", 4, lambda: sa.sigattn_fwd(q, k, v, nq, nk, a, b, out=o))]
+    if w.D == 64:
+        launches.append(("dkdv", 8, lambda: sa.sigattn_bwd_dkdv(q, k, v, do, nq, nk, a, b, dk=dk, dv=dv)))
+    else:
+        launches.append(("dk", 6, lambda: sa.sigattn_bwd_dk(q, k, v, do, nq, nk, a, b, dk=dk)))
+        launches.append(("dv", 4, lambda: sa.sigattn_bwd_dv(q, k, do, nq, nk, a, b, dv=dv)))
+    launches.append(("dq", 6, lambda: sa.sigattn_bwd_dq(q, k, v, do, nq, nk, a, b, dq=dq)))
+    nl = len(launches)
+
     def step(ev=None):
+        for i, (_, _, fn) in enumerate(launches):
+            if ev is not None:
+                ev[i].record(stream)
+            fn()
         if ev is not None:
-            ev[0].record(stream)
-        sa.sigattn_fwd(q, k, v, nq, nk, w.alpha, w.bias, out=o)
-        if ev is not None:
-            ev[1].record(stream)
-        sa.sigattn_bwd_dkdv(q, k, v, do, nq, nk, w.alpha, w.bias, dk=dk, dv=dv)
-        if ev is not None:
-            ev[2].record(stream)
-        sa.sigattn_bwd_dq(q, k, v, do, nq, nk, w.alpha, w.bias, dq=dq)
-        if ev is not None:
-            ev[3].record(stream)
+            ev[nl].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / steps
-    t_dkdv = sum(e[1].elapsed_time(e[2]) for e in events) / steps
-    t_dq = sum(e[2].elapsed_time(e[3]) for e in events) / steps
     fl = accounting.attention_flops(w.Z, w.L, w.H, w.D, inp["seqlens_q"], inp["seqlens_k"])
-    # Algorithmic contraction FLOPs of each kernel per valid score pair:
-    # fwd 4D (QK^T, PV), dK/dV 8D (S, dP, dV, dK), dQ 6D (S, dP, dQ).
     pairs = float((inp["seqlens_q"].astype("int64") * inp["seqlens_k"].astype("int64")).sum()) * w.H
-    kern = {
-        "fwd": {"ms": t_fwd, "flop": 4.0 * w.D * pairs},
-        "dkdv": {"ms": t_dkdv, "flop": 8.0 * w.D * pairs},
-        "dq": {"ms": t_dq, "flop": 6.0 * w.D * pairs},
-    }
+    kern = {}
+    for i, (name, per_pair, _) in enumerate(launches):
+        ms = sum(e[i].elapsed_time(e[i + 1]) for e in events) / steps
+        kern[name] = {"ms": ms, "flop": per_pair * w.D * pairs}
     for kv in kern.values():
         kv["tflops"] = kv["flop"] / (kv["ms"] * 1e-3) / 1e12
         kv["frac_peak"] = kv["tflops"] / PEAK_BF16_TFLOPS
+    t_fwd = kern["fwd"]["ms"]
+    t_bwd = sum(kv["ms"] for name, kv in kern.items() if name != "fwd")
     ms_step = elapsed / steps * 1e3
     res = {
         "workload": w,
@@ -117,9 +116,9 @@ def run_gpu(name, steps, warmup, seed=0):
         "tflops_valid": fl["total_valid"] / (ms_step * 1e-3) / 1e12,
         "tflops_padded": fl["total_padded"] / (ms_step * 1e-3) / 1e12,
         "fwd_tflops_valid": fl["fwd_valid"] / (t_fwd * 1e-3) / 1e12,
-        "bwd_tflops_valid": fl["bwd_valid"] / ((t_dkdv + t_dq) * 1e-3) / 1e12,
+        "bwd_tflops_valid": fl["bwd_valid"] / (t_bwd * 1e-3) / 1e12,
         "fwd_tflops_padded": fl["fwd_padded"] / (t_fwd * 1e-3) / 1e12,
-        "bwd_tflops_padded": fl["bwd_padded"] / ((t_dkdv + t_dq) * 1e-3) / 1e12,
+        "bwd_tflops_padded": fl["bwd_padded"] / (t_bwd * 1e-3) / 1e12,
         "kernels": kern,
         "flops": fl,
     }
@@ -166,6 +165,8 @@ def traffic_for(kernel_name: str, workload: str):
         rec = json.loads(TRAFFIC_FILE.read_text())
     except Exception:  # noqa: BLE001
         return None
+    from padding_aware_sigmoid_amd.profiling import kernel_source_hash
+
     if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
         return None
     k = rec.get("kernels", {}).get(kernel_name)
@@ -227,6 +228,15 @@ def main():
             "bwd_tflops_valid": round(pad_res["bwd_tflops_valid"], 2),
             "tflops_loss_vs_nopad": round(1.0 - pad_res["tflops_valid"] / main_res["tflops_valid"], 4),
         }
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        line["copy_bytes"] = args.copy_bytes
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

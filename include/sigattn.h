@@ -111,7 +111,8 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
 
 /*
  * The two halves of sigattn_bwd, for callers that want to place or time them
- * separately (for example, on two streams). Each launches one kernel.
+ * separately (for example, on two streams). sigattn_bwd_dq launches one kernel;
+ * sigattn_bwd_dkdv launches one at D = 64 and two (dk, then dv) at D = 128.
  * sigattn_bwd_dkdv writes dk and dv. sigattn_bwd_dq writes dq. Arguments are as
  * for sigattn_bwd. Together they compute exactly what sigattn_bwd computes,
  * bit for bit.
@@ -124,6 +125,23 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
                    const int32_t* seqlens_q, const int32_t* seqlens_k,
                    int Z, int L, int H, int D, float alpha, float bias, int dtype,
                    int32_t* tile_counts_dq, void* stream);
+
+/*
+ * dk alone and dv alone, each one kernel launch over the same key tiles as
+ * sigattn_bwd_dkdv (rainbus.top summary, 方法步骤详情 step 5: dV = P^T dO and
+ * dK = alpha dS^T Q are separate contractions over the recomputed P). dv needs
+ * no v. Both write tile_counts_dkdv as sigattn_bwd_dkdv does, and their outputs
+ * equal its dk and dv bit for bit. At D = 128, sigattn_bwd_dkdv is these two
+ * launches in sequence.
+ */
+int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                   const int32_t* seqlens_q, const int32_t* seqlens_k,
+                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts_dkdv, void* stream);
+int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv,
+                   const int32_t* seqlens_q, const int32_t* seqlens_k,
+                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts_dkdv, void* stream);
 
 /* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
  * backward (any other value) needs for this shape. 0 means none. */

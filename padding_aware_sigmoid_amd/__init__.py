@@ -8,8 +8,10 @@ from ._lib import BF16, FP32, KERNEL_DKDV, KERNEL_DQ, KERNEL_FWD, SigattnError, 
 from .ops import (  # noqa: F401
     SigmoidAttention,
     sigattn_bwd,
+    sigattn_bwd_dk,
     sigattn_bwd_dkdv,
     sigattn_bwd_dq,
+    sigattn_bwd_dv,
     sigattn_fwd,
     sigattn_tile_config,
     sigmoid_attention,

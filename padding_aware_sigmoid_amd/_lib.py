@@ -22,6 +22,8 @@ EXPORTED_SYMBOLS = (
     "sigattn_bwd",
     "sigattn_bwd_dkdv",
     "sigattn_bwd_dq",
+    "sigattn_bwd_dk",
+    "sigattn_bwd_dv",
     "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
@@ -56,6 +58,10 @@ def load():
     lib.sigattn_bwd_dkdv.restype = i32
     lib.sigattn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
     lib.sigattn_bwd_dq.restype = i32
+    lib.sigattn_bwd_dk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
+    lib.sigattn_bwd_dk.restype = i32
+    lib.sigattn_bwd_dv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
+    lib.sigattn_bwd_dv.restype = i32
     lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

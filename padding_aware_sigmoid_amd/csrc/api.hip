@@ -17,8 +17,8 @@ hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, const i
                            float, float, int32_t*, hipStream_t);
 #define SIGATTN_DECL_BWD(NAME)                                                                                   \
   template <int D>                                                                                               \
-  hipError_t NAME(const void*, const void*, const void*, const void*, void*, void*, const int32_t*, const int32_t*, \
-                  int, int, int, float, float, float, int32_t*, hipStream_t);
+  hipError_t NAME(int, const void*, const void*, const void*, const void*, void*, void*, const int32_t*,        \
+                  const int32_t*, int, int, int, float, float, float, int32_t*, hipStream_t);
 SIGATTN_DECL_BWD(launch_dkdv_bf16)
 SIGATTN_DECL_BWD(launch_dkdv_fp32)
 #define SIGATTN_DECL_DQ(NAME)                                                                                    \
@@ -90,21 +90,26 @@ int hip_status(hipError_t e) {
 // log2(e), for sigma(x) = 1 / (1 + 2^(-x log2 e))
 constexpr float kLog2e = 1.4426950408889634f;
 
+// What a dK/dV launch writes. The values match the kernels' KvMode.
+constexpr int kKvBoth = 0, kKvDk = 1, kKvDv = 2;
+
 }  // namespace
 
 namespace {
 
-int launch_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, const int32_t* nq,
-                const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype, int32_t* tc,
-                hipStream_t st) {
+int launch_dkdv(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                const int32_t* nq, const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                int32_t* tc, hipStream_t st) {
   const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipError_t e;
   if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dkdv_bf16<128>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64)
+            ? sigattn::launch_dkdv_bf16<64>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+            : sigattn::launch_dkdv_bf16<128>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
   else
-    e = (D == 64) ? sigattn::launch_dkdv_fp32<64>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dkdv_fp32<128>(q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64)
+            ? sigattn::launch_dkdv_fp32<64>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
+            : sigattn::launch_dkdv_fp32<128>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
   return hip_status(e);
 }
 
@@ -163,7 +168,7 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, v
       (rc = check_tensor(dv, "dv")))
     return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  rc = launch_dkdv(q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv, st);
+  rc = launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv, st);
   if (rc != SIGATTN_OK) return rc;
   return launch_dq(q, k, v, dout, dq, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dq, st);
 }
@@ -177,8 +182,34 @@ int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* do
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")))
     return rc;
-  return launch_dkdv(q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv,
-                     reinterpret_cast<hipStream_t>(stream));
+  return launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
+                     tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                   const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
+                   float bias, int dtype, int32_t* tile_counts_dkdv, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dk, "dk")))
+    return rc;
+  return launch_dkdv(kKvDk, q, k, v, dout, dk, nullptr, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
+                     tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv, const int32_t* seqlens_q,
+                   const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts_dkdv, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(dout, "dout")) ||
+      (rc = check_tensor(dv, "dv")))
+    return rc;
+  return launch_dkdv(kKvDv, q, k, nullptr, dout, nullptr, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
+                     tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,

@@ -38,10 +38,14 @@ struct BwdCfg {
 //   dP^T = V dO^T  (A = V from LDS)
 // dS^T = P (1 - P) dP^T is built in registers and fed as the A operand of
 // dQ += dS K. That product takes K from LDS through transposed reads.
-// Key tiles of 64 rows stream through a 2-slot LDS ring by DMA. Per 32-key
+// Key tiles of 64 rows stream through a 3-slot LDS ring by DMA. Per 32-key
 // block, the previous block's dQ MFMAs run beside this block's sigma and dS.
-// (A three-deep pipeline, like the dK/dV kernel's, needs more registers than
-// a wave has at D = 128. It spills, and it measured slower.)
+// Tile t-2 is last read in iteration t-1 (the dQ of its second block), so the
+// DMA of tile t+1 into its slot starts only after iteration t's barrier.
+// Each slot is its own LDS variable and the key loop is unrolled by three, so
+// every LDS access names its slot at compile time. The compiler can then tell
+// the in-flight DMA apart from the reads of the other two slots and does not
+// wait for it before them.
 template <int D>
 __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -50,8 +54,12 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
                                                       float alpha, float c1, float c0,
                                                       int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
   __shared__ int rank_lds[kMaxRankedSamples];
   const int n_qt = (L + C::BQ_DQ - 1) / C::BQ_DQ;
   const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, L, seqlens_q, seqlens_k, rank_lds);
@@ -93,25 +101,41 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
       for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
 
   const int nkt = (nk + C::BK_DQ - 1) / C::BK_DQ;
+  const int nkt3 = (nkt + 2) / 3 * 3;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Kb = K + base;
     const __bf16* Vb = V + base;
-    auto fetch = [&](int slot, int tile) {
+    auto fetch = [&](__bf16* sk, __bf16* sv, int tile) {
       const int k0 = tile * C::BK_DQ;
-      dma_tile<D, 64, 256>(sK[slot], Kb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
-      dma_tile<D, 64, 256>(sV[slot], Vb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+      const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
+      dma_tile<D, 64, 256>(sk, Kb + off, row_bytes, nk - k0, tid);
+      dma_tile<D, 64, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
-    fetch(0, 0);
+    // The dQ of the previous 32-key block, beside this block's sigma and dS.
+    auto dq_mfmas = [&](const __bf16* kt, int kbp, const bf16x8 (&dsp)[2][2]) {
+#pragma unroll
+      for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 b = lds_tr<D>(kt, kbp * 32 + ks * 16, db * 32, lane);
+          acc[0][db] = mfma32(dsp[0][ks], b, acc[0][db]);
+          acc[1][db] = mfma32(dsp[1][ks], b, acc[1][db]);
+        }
+    };
     // dS of the previous 32-key block, waiting for its dQ MFMAs (zero before the first block).
     bf16x8 ds_prev[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) ds_prev[qb][0] = ds_prev[qb][1] = zero_bf16x8();
-    int slot_prev = 0;
-    for (int t = 0; t < nkt; ++t) {
-      const int slot = t & 1;
+    // One key tile in slot S; slot P holds the tile before it, slot N receives the next.
+    auto iteration = [&](auto s_c, auto p_c, auto n_c, int t) {
+      constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
+      __bf16* const sk = ring<S>(sK0, sK1, sK2);
+      __bf16* const sv = ring<S>(sV0, sV1, sV2);
+      const __bf16* const skp = ring<P>(sK0, sK1, sK2);
       dma_wait();
-      __syncthreads();  // tile t is in LDS; every wave is done with tile t-1's dQ reads below
+      __syncthreads();  // tile t is in LDS, and every wave is done with iteration t-1
+      if (t + 1 < nkt3) fetch(ring<N>(sK0, sK1, sK2), ring<N>(sV0, sV1, sV2), t + 1);  // slot N held tile t-2
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // S^T, dP^T for this block (32 MFMAs)
@@ -122,27 +146,18 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
           for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 ak = lds_nat<D>(sK[slot], kb * 32 + l32, 2 * s + half);
-          const bf16x8 av = lds_nat<D>(sV[slot], kb * 32 + l32, 2 * s + half);
+          const bf16x8 ak = lds_nat<D>(sk, kb * 32 + l32, 2 * s + half);
+          const bf16x8 av = lds_nat<D>(sv, kb * 32 + l32, 2 * s + half);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
             sacc[qb] = mfma32(ak, qf[qb][s], sacc[qb]);
             pacc[qb] = mfma32(av, dof[qb][s], pacc[qb]);
           }
         }
-        // the previous block's dQ (16 MFMAs), beside this block's sigma and dS
-        {
-          const __bf16* kt = (kb == 0) ? sK[slot_prev] : sK[slot];
-          const int kbp = (kb == 0) ? 1 : 0;
-#pragma unroll
-          for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const bf16x8 b = lds_tr<D>(kt, kbp * 32 + ks * 16, db * 32, lane);
-              acc[0][db] = mfma32(ds_prev[0][ks], b, acc[0][db]);
-              acc[1][db] = mfma32(ds_prev[1][ks], b, acc[1][db]);
-            }
-        }
+        if (kb == 0)
+          dq_mfmas(skp, 1, ds_prev);
+        else
+          dq_mfmas(sk, 0, ds_prev);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -151,19 +166,24 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
             ds_prev[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
           }
         interleave_mfma_valu<4 * C::KS + 2 * C::NB * 2, 6>();
-        if (kb == 0 && t + 1 < nkt) fetch(slot ^ 1, t + 1);  // slot ^ 1 held tile t-1, finished above
       }
-      slot_prev = slot;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // Slot 2 stands in for tile -1: its reads are multiplied by ds_prev = 0, so
+    // it must hold finite values. It starts as zeros.
+    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sK2 + c * 8) = zero_bf16x8();
+    // The loop runs a multiple of three tiles. Tiles past n_k arrive as zeros
+    // (every DMA lane is out of range); a zero V row gives dP = 0 and so dS = 0,
+    // so they add exactly nothing.
+    fetch(sK0, sV0, 0);
+    for (int t = 0; t < nkt3; t += 3) {
+      iteration(I0{}, I2{}, I1{}, t);
+      iteration(I1{}, I0{}, I2{}, t + 1);
+      iteration(I2{}, I1{}, I0{}, t + 2);
     }
-    // dQ of the last block
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 b = lds_tr<D>(sK[slot_prev], 32 + ks * 16, db * 32, lane);
-        acc[0][db] = mfma32(ds_prev[0][ks], b, acc[0][db]);
-        acc[1][db] = mfma32(ds_prev[1][ks], b, acc[1][db]);
-      }
+    dq_mfmas(sK2, 1, ds_prev);  // the last block, of tile nkt3 - 1 (slot 2)
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -276,6 +296,17 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
   });
 }
 
+// Whether the dK/dV query loop is unrolled over the three ring slots. Unrolled,
+// every LDS access names its slot at compile time, and the compiler does not
+// wait for the DMA into one slot before reading the others. That costs a few
+// registers (slot addresses past the 64 KB read offset range need their own),
+// which the two kernels already at the register limit (fused dK+dV at D = 64,
+// dK at D = 128) cannot spare: they keep a runtime slot index, and the compiler
+// waits for each DMA before their next LDS read.
+template <int D, int MODE>
+constexpr bool kUnrolledRing = !(MODE == KV_BOTH || (MODE == KV_DK && D == 128));
+
+// One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV).
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -286,8 +317,12 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
                                                         int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
   constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ[3][C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sdO[3][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG2[C::TILE];
   __shared__ int rank_lds[kMaxRankedSamples];
   const int n_kt = (L + C::BK_KV - 1) / C::BK_KV;
   const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, L, seqlens_q, seqlens_k, rank_lds);
@@ -337,37 +372,67 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Qb = Q + base;
     const __bf16* dOb = dO + base;
-    auto fetch = [&](int slot, int tile) {
+    auto fetch = [&](__bf16* sq, __bf16* sg, int tile) {
       const int r0 = tile * C::BQ_KV;
-      dma_tile<D, 64, 256>(sQ[slot], Qb + (size_t)r0 * rs, row_bytes, nq - r0, tid);
-      dma_tile<D, 64, 256>(sdO[slot], dOb + (size_t)r0 * rs, row_bytes, nq - r0, tid);
+      const size_t off = (size_t)(r0 < nq ? r0 : 0) * rs;  // no row is read past n_q
+      dma_tile<D, 64, 256>(sq, Qb + off, row_bytes, nq - r0, tid);
+      dma_tile<D, 64, 256>(sg, dOb + off, row_bytes, nq - r0, tid);
     };
     f32x16 sX[2], pX[2], sY[2], pY[2];
     bf16x8 ptX[2][2], ptY[2][2], dsX[2][2], dsY[2][2];
-    fetch(0, 0);
-    dma_wait();
-    __syncthreads();
-    if (nqt > 1) fetch(1, 1);
-    kv_step<D, MODE, true, false, false>(sQ[0], sdO[0], 0, sQ[0], sdO[0], 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
-                                         dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
-    kv_step<D, MODE, true, false, true>(sQ[0], sdO[0], 1, sQ[0], sdO[0], 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX,
-                                        sX, pX, kf, vf, c1, c0, l32, half, lane);
-    int cur = 0, prev = 0;
-    for (int u = 1; u < nqt; ++u) {
-      prev = cur;
-      cur = (cur == 2) ? 0 : cur + 1;
+    // Query tile u: its slot (q_cur, g_cur), tile u-1's slot (q_prev, g_prev)
+    // and the slot that receives tile u+1 (it held tile u-2).
+    auto iteration = [&](__bf16* q_cur, __bf16* g_cur, __bf16* q_prev, __bf16* g_prev, __bf16* q_next,
+                         __bf16* g_next, int u, int n_tiles) {
       dma_wait();
       __syncthreads();
-      if (u + 1 < nqt) fetch(cur == 2 ? 0 : cur + 1, u + 1);
-      kv_step<D, MODE, true, true, true>(sQ[cur], sdO[cur], 0, sQ[prev], sdO[prev], 0, sX, pX, dkacc, dvacc, ptX,
-                                         dsX, ptY, dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
-      kv_step<D, MODE, true, true, true>(sQ[cur], sdO[cur], 1, sQ[prev], sdO[prev], 1, sY, pY, dkacc, dvacc, ptY,
-                                         dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
+      if (u + 1 < n_tiles) fetch(q_next, g_next, u + 1);
+      kv_step<D, MODE, true, true, true>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
+                                         dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
+      kv_step<D, MODE, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY, ptX,
+                                         dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
+    };
+    auto prologue = [&](int n_tiles) {
+      fetch(sQ0, sG0, 0);
+      dma_wait();
+      __syncthreads();
+      if (n_tiles > 1) fetch(sQ1, sG1, 1);  // no DMA may be left in flight when the kernel ends
+      kv_step<D, MODE, true, false, false>(sQ0, sG0, 0, sQ0, sG0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
+                                           pY, kf, vf, c1, c0, l32, half, lane);
+      kv_step<D, MODE, true, false, true>(sQ0, sG0, 1, sQ0, sG0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
+                                          pX, kf, vf, c1, c0, l32, half, lane);
+    };
+    auto epilogue = [&](__bf16* q_last, __bf16* g_last) {
+      kv_step<D, MODE, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
+                                          dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
+      kv_step<D, MODE, false, true, false>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY, dsY,
+                                           ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
+    };
+    if constexpr (kUnrolledRing<D, MODE>) {
+      // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
+      // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
+      // exactly nothing to dV or dK.
+      const int nqt3 = 1 + (nqt + 1) / 3 * 3;
+      prologue(nqt3);
+      for (int u = 1; u < nqt3; u += 3) {
+        iteration(sQ1, sG1, sQ0, sG0, sQ2, sG2, u, nqt3);
+        iteration(sQ2, sG2, sQ1, sG1, sQ0, sG0, u + 1, nqt3);
+        iteration(sQ0, sG0, sQ2, sG2, sQ1, sG1, u + 2, nqt3);
+      }
+      epilogue(sQ0, sG0);  // tile nqt3 - 1 sits in slot 0
+    } else {
+      auto q_at = [&](int i) { return i == 0 ? sQ0 : (i == 1 ? sQ1 : sQ2); };
+      auto g_at = [&](int i) { return i == 0 ? sG0 : (i == 1 ? sG1 : sG2); };
+      prologue(nqt);
+      int cur = 0;
+      for (int u = 1; u < nqt; ++u) {
+        const int prev = cur;
+        cur = (cur == 2) ? 0 : cur + 1;
+        const int next = (cur == 2) ? 0 : cur + 1;
+        iteration(q_at(cur), g_at(cur), q_at(prev), g_at(prev), q_at(next), g_at(next), u, nqt);
+      }
+      epilogue(q_at(cur), g_at(cur));
     }
-    kv_step<D, MODE, false, true, true>(sQ[cur], sdO[cur], 0, sQ[cur], sdO[cur], 0, sX, pX, dkacc, dvacc, ptX, dsX,
-                                        ptY, dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
-    kv_step<D, MODE, false, true, false>(sQ[cur], sdO[cur], 0, sQ[cur], sdO[cur], 1, sY, pY, dkacc, dvacc, ptY, dsY,
-                                         ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -470,7 +535,10 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
   const int tid = threadIdx.x, k0 = t * BK, row = k0 + tid;
   if (k0 >= nk) {
     if (row < L)
-      for (int d = 0; d < D; ++d) dK[base + (size_t)row * rs + d] = dV[base + (size_t)row * rs + d] = 0.0f;
+      for (int d = 0; d < D; ++d) {
+        if (dK != nullptr) dK[base + (size_t)row * rs + d] = 0.0f;
+        if (dV != nullptr) dV[base + (size_t)row * rs + d] = 0.0f;
+      }
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = 0;
     return;
   }
@@ -478,7 +546,8 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
   for (int c = tid; c < BK * D; c += 64) {
     const int r = c / D, d = c % D, kr = k0 + r;
     sKr[r][d] = kr < nk ? K[base + (size_t)kr * rs + d] : 0.0f;
-    sVr[r][d] = kr < nk ? V[base + (size_t)kr * rs + d] : 0.0f;
+    // V only feeds dK. A dV-only launch passes V = NULL.
+    sVr[r][d] = (kr < nk && dK != nullptr) ? V[base + (size_t)kr * rs + d] : 0.0f;
   }
   float dk[D], dv[D];
   for (int d = 0; d < D; ++d) dk[d] = dv[d] = 0.0f;
@@ -507,35 +576,33 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
   }
   if (row < L)
     for (int d = 0; d < D; ++d) {
-      dK[base + (size_t)row * rs + d] = live ? alpha * dk[d] : 0.0f;
-      dV[base + (size_t)row * rs + d] = live ? dv[d] : 0.0f;
+      if (dK != nullptr) dK[base + (size_t)row * rs + d] = live ? alpha * dk[d] : 0.0f;
+      if (dV != nullptr) dV[base + (size_t)row * rs + d] = live ? dv[d] : 0.0f;
     }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = nqt;
 }
 
 // --------------------------------------------------------------------------------- launchers
+// MODE: KV_BOTH (dk and dv), KV_DK (dk only) or KV_DV (dv only; v is not read).
 template <int D>
-hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                            const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1,
-                            float c0, int32_t* tc, hipStream_t st) {
+hipError_t launch_dkdv_bf16(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk,
+                            void* dv, const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha,
+                            float c1, float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
   const long long blocks = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
-  if constexpr (D == 64) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_BOTH>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
-                       H, alpha, c1, c0, tc);
-  } else {
-    // Both launches see the same lengths, so both write the same counters.
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DK>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
-                       H, alpha, c1, c0, tc);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DV>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L,
-                       H, alpha, c1, c0, tc);
-  }
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L, H, alpha, c1,
+                       c0, tc);
+    return hipGetLastError();
+  };
+  if (mode == KV_DK) return go(dkdv_bf16_kernel<D, KV_DK>);
+  if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV>);
+  if constexpr (D == 64) return go(dkdv_bf16_kernel<D, KV_BOTH>);
+  // D = 128: the fused form does not fit a wave's registers. Both launches see
+  // the same lengths, so both write the same counters.
+  hipError_t e = go(dkdv_bf16_kernel<D, KV_DK>);
+  return e != hipSuccess ? e : go(dkdv_bf16_kernel<D, KV_DV>);
 }
 
 template <int D>
@@ -550,9 +617,11 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
 }
 
 template <int D>
-hipError_t launch_dkdv_fp32(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                            const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha, float c1,
-                            float c0, int32_t* tc, hipStream_t st) {
+hipError_t launch_dkdv_fp32(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk,
+                            void* dv, const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha,
+                            float c1, float c0, int32_t* tc, hipStream_t st) {
+  if (mode == KV_DK) dv = nullptr;
+  if (mode == KV_DV) dk = nullptr;
   const long long blocks = (long long)Z * H * ((L + 63) / 64);
   hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
                      (const float*)v, (const float*)dout, (float*)dk, (float*)dv, nq, nk, L, H, alpha, c1, c0, tc);
@@ -570,13 +639,13 @@ hipError_t launch_dq_fp32(const void* q, const void* k, const void* v, const voi
 }
 
 #define SIGATTN_INST_BWD(D)                                                                                   \
-  template hipError_t launch_dkdv_bf16<D>(const void*, const void*, const void*, const void*, void*, void*,      \
+  template hipError_t launch_dkdv_bf16<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
                                           const int32_t*, const int32_t*, int, int, int, float, float, float,  \
                                           int32_t*, hipStream_t);                                              \
   template hipError_t launch_dq_bf16<D>(const void*, const void*, const void*, const void*, void*,              \
                                         const int32_t*, const int32_t*, int, int, int, float, float, float,    \
                                         int32_t*, hipStream_t);                                                \
-  template hipError_t launch_dkdv_fp32<D>(const void*, const void*, const void*, const void*, void*, void*,      \
+  template hipError_t launch_dkdv_fp32<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
                                           const int32_t*, const int32_t*, int, int, int, float, float, float,  \
                                           int32_t*, hipStream_t);                                              \
   template hipError_t launch_dq_fp32<D>(const void*, const void*, const void*, const void*, void*,              \

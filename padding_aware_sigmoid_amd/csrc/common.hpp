@@ -89,6 +89,19 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+// Slot I of a ring of three LDS buffers, chosen at compile time. Each slot is
+// its own __shared__ variable. An access through the returned pointer is then
+// known to touch only that variable, which lets the compiler tell a DMA into
+// one slot apart from reads of another (it waits for an LDS DMA before any LDS
+// read it cannot prove disjoint from it).
+template <int I, typename T>
+__device__ __forceinline__ T* ring(T* a, T* b, T* c) {
+  static_assert(I >= 0 && I < 3, "ring slot out of range");
+  if constexpr (I == 0) return a;
+  else if constexpr (I == 1) return b;
+  else return c;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = BEGIN .. END-1.
 // The index is a constant expression inside f, which the scheduling builtins
 // need.

@@ -138,7 +138,10 @@ __device__ __forceinline__ void fwd_phase(f32x16 (&s_out)[2], const __bf16* sK, 
 //   phase B: S(t+1, 1st half) and O += P(t, 1st half) V   ||   P(t, 2nd half) = sigma(S)
 // The LDS ring holds tiles t-1, t and t+1. There is one barrier per key tile.
 // K and V come straight from global memory into LDS by DMA, with padded key
-// rows replaced by zeros on the way.
+// rows replaced by zeros on the way. Each ring slot is its own LDS variable
+// and the key loop is unrolled by three, so every access names its slot at
+// compile time; the compiler then sees that phase B's reads cannot touch the
+// slot the DMA is filling and does not wait for the DMA before them.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -146,8 +149,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
                                                        const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
                                                        float c1, float c0, int32_t* __restrict__ tile_counts) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[C::NBUF][C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV[C::NBUF][C::TILE];
+  static_assert(C::NBUF == 3, "the key loop is unrolled over a ring of three slots");
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
 
   __shared__ int rank_lds[kMaxRankedSamples];
   const int n_qt = (L + C::BQ - 1) / C::BQ;
@@ -188,20 +196,25 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
 
   const int nkt = (nk + C::BK - 1) / C::BK;
+  // The loop runs a multiple of three tiles. Tiles past n_k arrive as zeros
+  // (every DMA lane is out of range): their V rows are 0, so they add exactly
+  // nothing to O.
+  const int nkt3 = (nkt + 2) / 3 * 3;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Kb = K + base;
     const __bf16* Vb = V + base;
-    auto fetch = [&](int slot, int tile) {  // DMA key tile `tile` into LDS slot `slot`
+    auto fetch = [&](__bf16* sk, __bf16* sv, int tile) {  // DMA key tile `tile` into one slot
       const int k0 = tile * C::BK;
-      dma_tile<D, C::BK, 256>(sK[slot], Kb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
-      dma_tile<D, C::BK, 256>(sV[slot], Vb + (size_t)k0 * rs, row_bytes, nk - k0, tid);
+      const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
+      dma_tile<D, C::BK, 256>(sk, Kb + off, row_bytes, nk - k0, tid);
+      dma_tile<D, C::BK, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
-    fetch(0, 0);
-    if (nkt > 1) fetch(1, 1);
+    fetch(sK0, sV0, 0);
+    fetch(sK1, sV1, 1);
     // Slot 2's V is read by the first phase A with P = 0 (there is no tile -1).
     // It must hold finite values then, so it starts as zeros.
-    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sV[2] + c * 8) = zero_bf16x8();
+    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sV2 + c * 8) = zero_bf16x8();
     dma_wait();
     __syncthreads();
 
@@ -209,23 +222,31 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
     bf16x8 p0[2][2], p1[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) p1[qb][0] = p1[qb][1] = zero_bf16x8();
-    scores_t<D>(s_cur, sK[0], 0, qf, l32, half);
-    int bt = 0;  // LDS slot of tile t
-    for (int t = 0; t < nkt; ++t) {
-      const int bprev = (bt == 0) ? C::NBUF - 1 : bt - 1;
-      const int bnext = (bt == C::NBUF - 1) ? 0 : bt + 1;
+    scores_t<D>(s_cur, sK0, 0, qf, l32, half);
+    // Key tile t in slot T; slot P holds tile t-1 and slot N tile t+1.
+    auto iteration = [&](auto t_c, auto p_c, auto n_c, int t) {
+      constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
       // phase A: 32 MFMAs beside 32 sigmoids per lane
-      fwd_phase<D>(s_nxt, sK[bt], 1, oacc, p1, sV[bprev], 1, p0, s_cur, qf, c1, c0, l32, half, lane);
+      fwd_phase<D>(s_nxt, ring<T>(sK0, sK1, sK2), 1, oacc, p1, ring<P>(sV0, sV1, sV2), 1, p0, s_cur, qf, c1, c0,
+                   l32, half, lane);
       pin_before_barrier(p0);
       dma_wait();       // this wave's DMA of tile t+1 has landed
-      __syncthreads();  // ... everyone's has, and every wave is done with slot bprev
-      if (t + 2 < nkt) fetch(bprev, t + 2);
-      // phase B. When t + 1 == nkt the new S is computed from a stale slot and is never used.
-      fwd_phase<D>(s_cur, sK[bnext], 0, oacc, p0, sV[bt], 0, p1, s_nxt, qf, c1, c0, l32, half, lane);
-      bt = bnext;
+      __syncthreads();  // ... everyone's has, and every wave is done with slot P
+      if (t + 2 < nkt3) fetch(ring<P>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), t + 2);
+      // phase B. At the last tile the new S comes from a stale slot and is never used.
+      fwd_phase<D>(s_cur, ring<N>(sK0, sK1, sK2), 0, oacc, p0, ring<T>(sV0, sV1, sV2), 0, p1, s_nxt, qf, c1, c0,
+                   l32, half, lane);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int t = 0; t < nkt3; t += 3) {
+      iteration(I0{}, I2{}, I1{}, t);
+      iteration(I1{}, I0{}, I2{}, t + 1);
+      iteration(I2{}, I1{}, I0{}, t + 2);
     }
-    // the last tile's second half
-    accumulate_pv<D>(oacc, p1, sV[bt == 0 ? C::NBUF - 1 : bt - 1], 1, lane);
+    // the second half of tile nkt3 - 1 (slot 2)
+    accumulate_pv<D>(oacc, p1, sV2, 1, lane);
   }
 
   // Epilogue. Register r of oacc[qb][db] holds query row 64w + 32qb + acc_row(r, half), column 32db + l%32.

@@ -145,6 +145,40 @@ def sigattn_bwd_dq(q, k, v, dout, seqlens_q, seqlens_k, alpha=None, bias=None, d
     return dq
 
 
+def sigattn_bwd_dk(q, k, v, dout, seqlens_q, seqlens_k, alpha=None, bias=None, dk=None, tile_counts_dkdv=None):
+    """dk only: one kernel launch. Wraps the C entry point sigattn_bwd_dk."""
+    _check_tensors(q, {"k": k, "v": v, "dout": dout})
+    Z, L, H, D = q.shape
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(L) if bias is None else float(bias)
+    nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
+    dk = torch.empty_like(q) if dk is None else dk
+    _check_tensors(q, {"dk": dk})
+    lib = _lib.load()
+    _lib.check(lib.sigattn_bwd_dk(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dk.data_ptr(),
+                                  nq.data_ptr(), nk.data_ptr(), Z, L, H, D, alpha, bias, _dtype_code(q),
+                                  None if tile_counts_dkdv is None else tile_counts_dkdv.data_ptr(),
+                                  _stream(q.device)))
+    return dk
+
+
+def sigattn_bwd_dv(q, k, dout, seqlens_q, seqlens_k, alpha=None, bias=None, dv=None, tile_counts_dkdv=None):
+    """dv only (v is not needed): one kernel launch. Wraps the C entry point sigattn_bwd_dv."""
+    _check_tensors(q, {"k": k, "dout": dout})
+    Z, L, H, D = q.shape
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(L) if bias is None else float(bias)
+    nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_tensors(q, {"dv": dv})
+    lib = _lib.load()
+    _lib.check(lib.sigattn_bwd_dv(q.data_ptr(), k.data_ptr(), dout.data_ptr(), dv.data_ptr(), nq.data_ptr(),
+                                  nk.data_ptr(), Z, L, H, D, alpha, bias, _dtype_code(q),
+                                  None if tile_counts_dkdv is None else tile_counts_dkdv.data_ptr(),
+                                  _stream(q.device)))
+    return dv
+
+
 def sigattn_tile_config(kernel: int, D: int, dtype) -> tuple:
     code = dtype if isinstance(dtype, int) else _DTYPES[dtype]
     return _lib.tile_config(kernel, D, code)

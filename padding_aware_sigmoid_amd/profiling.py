@@ -1,0 +1,153 @@
+"""Summaries of rocprofv3 output for the sigattn kernels.
+
+    python -m padding_aware_sigmoid_amd.profiling stats    TRACE_DIR  [-o OUT.md]
+    python -m padding_aware_sigmoid_amd.profiling counters PMC_DIR... [-o OUT.md]
+    python -m padding_aware_sigmoid_amd.profiling traffic  --fetch DIR --write DIR --workload NAME
+                                                           --copy-bytes N [-o OUT.json]
+
+`stats` tabulates a `--kernel-trace --stats` run (per-kernel calls and
+durations). `counters` tabulates `--pmc` runs: each counter's mean per
+dispatch, per kernel. `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run
+into HBM bytes per launch. Each counter is scaled by the factor that makes it
+read the known size of a plain device copy recorded in the same run
+(`bench.py --copy-bytes N`). The JSON carries a hash of the kernel sources, so
+a reader can tell when the kernels have changed since the counters were taken.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import pathlib
+import re
+import sys
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+KERNEL_SOURCES = ["padding_aware_sigmoid_amd/csrc/common.hpp", "padding_aware_sigmoid_amd/csrc/fwd.hip",
+                  "padding_aware_sigmoid_amd/csrc/bwd.hip"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update((ROOT / p).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str | None:
+    """The bench name of a sigattn kernel from its demangled name, else None."""
+    m = re.search(r"sigattn::(fwd|dq|dkdv)_(bf16|fp32)_kernel<(\d+)(?:,\s*(\d))?>", kernel)
+    if m is None:
+        return None
+    kind, dtype, _, mode = m.groups()
+    if kind == "dkdv" and mode is not None:
+        kind = {"0": "dkdv", "1": "dk", "2": "dv"}[mode]
+    return kind if dtype == "bf16" else f"{kind}_fp32"
+
+
+def _csv(path: pathlib.Path, suffix: str) -> list[dict]:
+    files = sorted(path.rglob(f"*{suffix}")) if path.is_dir() else [path]
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {path}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def stats_table(trace_dir: pathlib.Path) -> str:
+    rows = _csv(trace_dir, "kernel_stats.csv")
+    out = ["| kernel | calls | avg ms | min ms | max ms | share of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = short_name(r["Name"]) or r["Name"][:48]
+        out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | {float(r['MinNs']) / 1e6:.4f} | "
+                   f"{float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(out)
+
+
+def counter_means(pmc_dirs: list[pathlib.Path]) -> dict:
+    """{kernel: {counter: mean per dispatch}} over the sigattn kernels (and the copy kernel)."""
+    acc: dict = {}
+    for d in pmc_dirs:
+        for r in _csv(d, "counter_collection.csv"):
+            name = short_name(r["Kernel_Name"]) or (COPY_KERNEL if COPY_KERNEL in r["Kernel_Name"] else None)
+            if name is None:
+                continue
+            acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters_table(pmc_dirs: list[pathlib.Path]) -> str:
+    means = counter_means(pmc_dirs)
+    names = sorted({c for cs in means.values() for c in cs})
+    out = ["| kernel | " + " | ".join(names) + " |", "|---|" + "---:|" * len(names)]
+    for k, cs in means.items():
+        if k == COPY_KERNEL:
+            continue
+        out.append(f"| {k} | " + " | ".join(f"{cs[c]:.4g}" if c in cs else "" for c in names) + " |")
+    return "\n".join(out)
+
+
+def _copy_factor(rows: list[dict], counter: str, copy_bytes: int) -> float:
+    """Known bytes / counted bytes for the calibration copy: the copy-kernel
+    dispatches with the largest grid in the run (the inputs' own small copies
+    have far smaller grids)."""
+    copies = [r for r in rows if COPY_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not copies:
+        raise ValueError(f"no {COPY_KERNEL} dispatch in the {counter} run")
+    g = max(int(r["Grid_Size"]) for r in copies)
+    vals = [float(r["Counter_Value"]) * 1024 for r in copies if int(r["Grid_Size"]) == g]
+    return copy_bytes / (sum(vals) / len(vals))
+
+
+def traffic(fetch_dir: pathlib.Path, write_dir: pathlib.Path, workload: str, copy_bytes: int) -> dict:
+    frows = _csv(fetch_dir, "counter_collection.csv")
+    wrows = _csv(write_dir, "counter_collection.csv")
+    f_fac = _copy_factor(frows, "FETCH_SIZE", copy_bytes)
+    w_fac = _copy_factor(wrows, "WRITE_SIZE", copy_bytes)
+    means = counter_means([fetch_dir, write_dir])
+    kernels = {}
+    for k, cs in means.items():
+        if k == COPY_KERNEL or "FETCH_SIZE" not in cs or "WRITE_SIZE" not in cs:
+            continue
+        fb, wb = cs["FETCH_SIZE"] * 1024 * f_fac, cs["WRITE_SIZE"] * 1024 * w_fac
+        kernels[k] = {"fetch_kib_raw": round(cs["FETCH_SIZE"], 2), "write_kib_raw": round(cs["WRITE_SIZE"], 2),
+                      "fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    return {"kernel_source_hash": kernel_source_hash(), "workload": workload, "copy_bytes": copy_bytes,
+            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": kernels}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("trace_dir", type=pathlib.Path)
+    a.add_argument("-o", type=pathlib.Path)
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dirs", type=pathlib.Path, nargs="+")
+    c.add_argument("-o", type=pathlib.Path)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", type=pathlib.Path, required=True)
+    t.add_argument("--write", type=pathlib.Path, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("-o", type=pathlib.Path)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        text = stats_table(args.trace_dir)
+    elif args.cmd == "counters":
+        text = counters_table(args.pmc_dirs)
+    else:
+        text = json.dumps(traffic(args.fetch, args.write, args.workload, args.copy_bytes), indent=1)
+    if args.o:
+        args.o.write_text(text + "\n")
+    else:
+        sys.stdout.write(text + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -151,17 +151,27 @@ def test_empty_and_errors():
     assert torch.all(torch.isfinite(out)) and torch.all(out[:, 50:] == 0)
 
 
-def test_split_backward_entry_points_match():
-    """sigattn_bwd_dkdv + sigattn_bwd_dq give exactly what sigattn_bwd gives."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_backward_entry_points_match(dtype, D):
+    """sigattn_bwd_dkdv + sigattn_bwd_dq, and sigattn_bwd_dk + sigattn_bwd_dv,
+    give exactly what sigattn_bwd gives, counters included."""
     import padding_aware_sigmoid_amd as sa
 
-    Z, L, H, D = 2, 300, 2, 128
+    Z, L, H = 2, 300, 2
     n = np.array([300, 123])
-    note("split backward entry points")
-    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=10)
+    note(f"split backward entry points {dtype} D={D}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, dtype, seed=10)
     dq_, dk_, dv_, ddo, dn, _ = device_inputs(q, k, v, do, n, n)
-    a = sa.sigattn_bwd(dq_, dk_, dv_, ddo, dn, dn)
+    _, bk = sa.sigattn_tile_config(sa.KERNEL_DKDV, D, dq_.dtype)
+    ntk = Z * H * (-(-L // bk))
+    c0, c1, c2 = (torch.full((ntk,), -7, dtype=torch.int32, device=dq_.device) for _ in range(3))
+    a = sa.sigattn_bwd(dq_, dk_, dv_, ddo, dn, dn, tile_counts_dkdv=c0)
     gk, gv = sa.sigattn_bwd_dkdv(dq_, dk_, dv_, ddo, dn, dn)
     gq = sa.sigattn_bwd_dq(dq_, dk_, dv_, ddo, dn, dn)
+    hk = sa.sigattn_bwd_dk(dq_, dk_, dv_, ddo, dn, dn, tile_counts_dkdv=c1)
+    hv = sa.sigattn_bwd_dv(dq_, dk_, ddo, dn, dn, tile_counts_dkdv=c2)
     torch.cuda.synchronize()
     assert torch.equal(a[0], gq) and torch.equal(a[1], gk) and torch.equal(a[2], gv)
+    assert torch.equal(a[1], hk) and torch.equal(a[2], hv)
+    assert torch.equal(c0, c1) and torch.equal(c0, c2) and int(c0.min()) >= 0
