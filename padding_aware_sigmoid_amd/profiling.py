@@ -81,6 +81,22 @@ def counter_means(pmc_dirs: list[pathlib.Path]) -> dict:
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
 
 
+# Ratios read off the SQ counters. SQ_WAVE_CYCLES, SQ_WAIT_ANY and
+# SQ_ACTIVE_INST_VALU count wave-cycles in units of 4 clocks;
+# SQ_VALU_MFMA_BUSY_CYCLES counts SIMD clocks. With one wave per SIMD (every
+# bf16 kernel here), 4 * SQ_WAVE_CYCLES is the SIMD clocks the waves were
+# resident, so the MFMA-busy fraction needs no assumption about the clock.
+DERIVED = (
+    ("VALU instr / MFMA", ("SQ_INSTS_VALU", "SQ_INSTS_MFMA"), lambda a, b: a / b),
+    ("transcendental instr / MFMA", ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"), lambda a, b: a / b),
+    ("LDS instr / MFMA", ("SQ_INSTS_LDS", "SQ_INSTS_MFMA"), lambda a, b: a / b),
+    ("MFMA busy / SIMD clocks", ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVE_CYCLES"), lambda a, b: a / (4 * b)),
+    ("VALU active / wave cycles", ("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"), lambda a, b: a / b),
+    ("waiting / wave cycles", ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"), lambda a, b: a / b),
+    ("LDS bank conflicts / LDS active", ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"), lambda a, b: a / b),
+)
+
+
 def counters_table(pmc_dirs: list[pathlib.Path]) -> str:
     means = counter_means(pmc_dirs)
     names = sorted({c for cs in means.values() for c in cs})
@@ -89,6 +105,18 @@ def counters_table(pmc_dirs: list[pathlib.Path]) -> str:
         if k == COPY_KERNEL:
             continue
         out.append(f"| {k} | " + " | ".join(f"{cs[c]:.4g}" if c in cs else "" for c in names) + " |")
+    rows = [(label, f) for label, need, f in DERIVED if all(n in names for n in need)]
+    if rows:
+        kernels = [k for k in means if k != COPY_KERNEL]
+        out += ["", "| ratio | " + " | ".join(kernels) + " |", "|---|" + "---:|" * len(kernels)]
+        for label, need, f in DERIVED:
+            if not all(n in names for n in need):
+                continue
+            vals = []
+            for k in kernels:
+                a, b = (means[k].get(n) for n in need)
+                vals.append("" if a is None or not b else f"{f(a, b):.3f}")
+            out.append(f"| {label} | " + " | ".join(vals) + " |")
     return "\n".join(out)
 
 
