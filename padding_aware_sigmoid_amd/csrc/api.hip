@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/sigattn.h"
+#include "sigattn.h"
 
 namespace sigattn {
 template <int D>

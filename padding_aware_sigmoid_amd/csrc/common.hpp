@@ -307,6 +307,28 @@ __device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* rows, uint3
   }
 }
 
+// One of dma_tile's (ROWS * D / 8) / NTHREADS DMA instructions per thread,
+// chunk i, so that a tile's DMA can be spread over a step schedule instead of
+// issued in one burst. Calling every i in 0 .. kDmaChunks - 1 equals dma_tile.
+template <int D, int ROWS, int NTHREADS>
+constexpr int kDmaChunks = ROWS * Tile<D>::CPR / NTHREADS;
+
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void dma_tile_chunk(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid,
+                                               int tid, int i) {
+  constexpr int CPR = Tile<D>::CPR;
+  const int nv = n_valid < 0 ? 0 : (n_valid > ROWS ? ROWS : n_valid);
+  const i32x4 rsrc = make_rsrc(rows, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
+  const int lane = tid & 63, wbase = tid & ~63;
+  const int P0 = i * NTHREADS + wbase;  // wave-uniform first slot
+  const int P = P0 + lane;
+  const int r = P / CPR, cs = P % CPR;
+  const int c = cs ^ Tile<D>::swz(r);
+  const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16), 16,
+                                  (int)voff, 0, 0, 0);
+}
+
 // Wait until this wave's outstanding global loads (the DMAs included) are done.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 

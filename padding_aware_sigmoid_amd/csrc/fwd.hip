@@ -77,71 +77,115 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], 
     }
 }
 
-// One pipeline phase of the forward for one wave, written as a fixed step
-// schedule. With one wave per SIMD, latency can only be hidden inside the
-// wave's own instruction stream.
-// The phase does three independent jobs:
-//   S_out = K(kb_s) Q^T   (KS steps of 2 MFMAs; A operand = a K row chunk)
-//   O += P_in V(kb_v)     (2*NB steps of 2 MFMAs; B operand = a V tr-read pair)
-//   P_out = sigma(S_in)   (32 values per lane, spread evenly over the steps)
-// The LDS operand of step j+2 is requested at step j (a 3-deep ring of
-// operand registers). An MFMA therefore never waits on a read issued just
-// before it, and the sigma work fills the MFMA pipe's busy cycles.
-template <int D>
-__device__ __forceinline__ void fwd_phase(f32x16 (&s_out)[2], const __bf16* sK, int kb_s,
-                                          f32x16 (&oacc)[2][FwdCfg<D>::NB], const bf16x8 (&p_in)[2][2],
-                                          const __bf16* sV, int kb_v, bf16x8 (&p_out)[2][2], const f32x16 (&s_in)[2],
-                                          const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0, int l32,
-                                          int half, int lane) {
+// One key tile of the forward for one wave, written as a fixed step schedule.
+// With one wave per SIMD, latency can only be hidden inside the wave's own
+// instruction stream. The tile is two phases of NSTEP steps, 2 MFMAs each:
+//   phase A: S(t, 2nd half) = K Q^T (KS steps), then O += P(t-1, 2nd half) V
+//            (2*NB steps)                          || P(t, 1st half) = sigma(S)
+//   barrier (at_barrier: the DMA of tile t+1 has landed; the next one starts)
+//   phase B: O += P(t, 1st half) V (2*NB steps), then S(t+1, 1st half)
+//            (KS steps)                            || P(t, 2nd half) = sigma(S)
+// The LDS operand of step g+3 is requested at step g, through the barrier and
+// on into the next tile's first steps. Reads that precede the barrier touch
+// only V of tile t, which landed a tile earlier; tile t+1's K is read only after
+// the barrier. Phase B puts P V first so those early reads exist. Since S of
+// phase B is finished by its last steps, phase A's sigma starts one step late.
+// ops[0..2] hold the operands of steps 0..2 on entry and of the next tile's
+// steps 0..2 on exit (2 * NSTEP is a multiple of 4, the ring depth).
+template <int D, typename AtBarrier, typename DmaChunk>
+__device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
+                                         f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                         f32x16 (&oacc)[2][FwdCfg<D>::NB], bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
+                                         bf16x8 (&ops)[4], const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0,
+                                         int l32, int half, int lane, AtBarrier&& at_barrier, DmaChunk&& dma_chunk) {
   using C = FwdCfg<D>;
-  constexpr int NSTEP = C::KS + 2 * C::NB;  // 16 at D = 128, 8 at D = 64
-  constexpr int EPS = 32 / NSTEP;           // sigma values per step
-  auto read = [&](auto jc) -> bf16x8 {
-    constexpr int j = decltype(jc)::value;
-    if constexpr (j < C::KS) {
-      return lds_nat<D>(sK, kb_s * 32 + l32, 2 * j + half);
+  constexpr int KS = C::KS, NB2 = 2 * C::NB;
+  constexpr int NSTEP = KS + NB2;  // steps per phase: 16 at D = 128, 8 at D = 64
+  constexpr int G = 2 * NSTEP;     // steps per tile
+  static_assert(G % 4 == 0 && KS >= 3 && NB2 >= 3, "ring of four operands, three steps ahead");
+  // The next DMA is NDMA instructions per thread (K and V), spread one per
+  // DSTRIDE steps over phase B: issued in one burst they stall the wave.
+  constexpr int NDMA = 2 * kDmaChunks<D, C::BK, 256>;
+  constexpr int DSTRIDE = NSTEP / NDMA > 0 ? NSTEP / NDMA : 1;
+  static_assert(NDMA <= NSTEP, "one DMA instruction per step at most");
+  // The operand of step g; g >= G are the next tile's first steps (K of tile t+1, 2nd half).
+  auto read = [&](auto gc) -> bf16x8 {
+    constexpr int g = decltype(gc)::value;
+    if constexpr (g < KS) {
+      return lds_nat<D>(kT, 32 + l32, 2 * g + half);
+    } else if constexpr (g < NSTEP) {
+      constexpr int i = g - KS;
+      return lds_tr<D>(vP, 32 + (i & 1) * 16, (i >> 1) * 32, lane);
+    } else if constexpr (g < NSTEP + NB2) {
+      constexpr int i = g - NSTEP;
+      return lds_tr<D>(vT, (i & 1) * 16, (i >> 1) * 32, lane);
+    } else if constexpr (g < G) {
+      return lds_nat<D>(kN, l32, 2 * (g - NSTEP - NB2) + half);
     } else {
-      constexpr int i = j - C::KS;
-      return lds_tr<D>(sV, kb_v * 32 + (i & 1) * 16, (i >> 1) * 32, lane);
+      return lds_nat<D>(kN, 32 + l32, 2 * (g - G) + half);
     }
   };
+  auto reads_of = [](int g) constexpr -> int {  // LDS instructions behind step g's operand
+    const int h = g % G;
+    return (h < KS || h >= NSTEP + NB2) ? 1 : 2;
+  };
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s_out[0][r] = s_out[1][r] = 0.0f;
-  bf16x8 ops[3];
-  ops[0] = read(std::integral_constant<int, 0>{});
-  ops[1] = read(std::integral_constant<int, 1>{});
-  static_for<0, NSTEP>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    if constexpr (j + 2 < NSTEP) ops[(j + 2) % 3] = read(std::integral_constant<int, j + 2>{});
-    const bf16x8 op = ops[j % 3];
-    if constexpr (j < C::KS) {
-      s_out[0] = mfma32(op, qf[0][j], s_out[0]);
-      s_out[1] = mfma32(op, qf[1][j], s_out[1]);
-    } else {
-      constexpr int i = j - C::KS, db = i >> 1, ks = i & 1;
-      oacc[0][db] = mfma32(p_in[0][ks], op, oacc[0][db]);
-      oacc[1][db] = mfma32(p_in[1][ks], op, oacc[1][db]);
+  for (int r = 0; r < 16; ++r) s_nxt[0][r] = s_nxt[1][r] = 0.0f;
+  static_for<0, G>([&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    if constexpr (g == NSTEP) {
+      pin_before_barrier(p0);
+      at_barrier();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_cur[0][r] = s_cur[1][r] = 0.0f;
     }
-    static_for<j * EPS, (j + 1) * EPS>([&](auto ec) {
+    ops[(g + 3) % 4] = read(std::integral_constant<int, g + 3>{});
+    const bf16x8 op = ops[g % 4];
+    if constexpr (g < KS) {
+      s_nxt[0] = mfma32(op, qf[0][g], s_nxt[0]);
+      s_nxt[1] = mfma32(op, qf[1][g], s_nxt[1]);
+    } else if constexpr (g < NSTEP) {
+      constexpr int i = g - KS, db = i >> 1, ks = i & 1;
+      oacc[0][db] = mfma32(p1[0][ks], op, oacc[0][db]);
+      oacc[1][db] = mfma32(p1[1][ks], op, oacc[1][db]);
+    } else if constexpr (g < NSTEP + NB2) {
+      constexpr int i = g - NSTEP, db = i >> 1, ks = i & 1;
+      oacc[0][db] = mfma32(p0[0][ks], op, oacc[0][db]);
+      oacc[1][db] = mfma32(p0[1][ks], op, oacc[1][db]);
+    } else {
+      constexpr int s = g - NSTEP - NB2;
+      s_cur[0] = mfma32(op, qf[0][s], s_cur[0]);
+      s_cur[1] = mfma32(op, qf[1][s], s_cur[1]);
+    }
+    // sigma: phase A turns S(t, 1st half) into p0 over steps 1..NSTEP-1,
+    // phase B turns S(t, 2nd half) into p1 over steps 0..NSTEP-1.
+    constexpr int e0 = g < NSTEP ? (g == 0 ? 0 : (g - 1) * 32 / (NSTEP - 1)) : (g - NSTEP) * 32 / NSTEP;
+    constexpr int e1 = g < NSTEP ? (g == 0 ? 0 : g * 32 / (NSTEP - 1)) : (g - NSTEP + 1) * 32 / NSTEP;
+    static_for<e0, e1>([&](auto ec) {
       constexpr int e = decltype(ec)::value, qb = e >> 4, r = e & 15;
-      p_out[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_in[qb][r], c1, c0);
+      if constexpr (g < NSTEP)
+        p0[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_cur[qb][r], c1, c0);
+      else
+        p1[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_nxt[qb][r], c1, c0);
     });
-    sched_step<j, (j + 2 < NSTEP) ? ((j + 2 < C::KS) ? 1 : 2) : 0, 2, 5 * EPS, 2>();
+    constexpr bool dma_here = g >= NSTEP && (g - NSTEP) % DSTRIDE == 0 && (g - NSTEP) / DSTRIDE < NDMA;
+    if constexpr (dma_here) {
+      dma_chunk((g - NSTEP) / DSTRIDE);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // the DMA first in its step
+    }
+    sched_step<g, reads_of(g + 3), 2, 5 * (e1 - e0), 2>();
   });
 }
 
 // Forward. Each wave owns 64 query rows. The key loop is software-pipelined in
 // half-tiles (32 keys) so that the MFMAs of one half-tile run beside the sigma
-// of another. In key tile t:
-//   phase A: S(t, 2nd half) and O += P(t-1, 2nd half) V   ||   P(t, 1st half) = sigma(S)
-//   barrier; the DMA of tile t+2 into the slot tile t-1 held starts
-//   phase B: S(t+1, 1st half) and O += P(t, 1st half) V   ||   P(t, 2nd half) = sigma(S)
-// The LDS ring holds tiles t-1, t and t+1. There is one barrier per key tile.
-// K and V come straight from global memory into LDS by DMA, with padded key
-// rows replaced by zeros on the way. Each ring slot is its own LDS variable
-// and the key loop is unrolled by three, so every access names its slot at
-// compile time; the compiler then sees that phase B's reads cannot touch the
-// slot the DMA is filling and does not wait for the DMA before them.
+// of another (fwd_tile). The LDS ring holds tiles t-1, t and t+1, and there is
+// one barrier per key tile. K and V come straight from global memory into LDS
+// by DMA, with padded key rows replaced by zeros on the way. Each ring slot is
+// its own LDS variable and the key loop is unrolled by three, so every access
+// names its slot at compile time; the compiler then sees that the reads after
+// the barrier cannot touch the slot the DMA is filling and does not wait for
+// the DMA before them.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -219,23 +263,33 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
     __syncthreads();
 
     f32x16 s_cur[2], s_nxt[2];
-    bf16x8 p0[2][2], p1[2][2];
+    bf16x8 p0[2][2], p1[2][2], ops[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) p1[qb][0] = p1[qb][1] = zero_bf16x8();
     scores_t<D>(s_cur, sK0, 0, qf, l32, half);
+#pragma unroll
+    for (int s3 = 0; s3 < 3; ++s3) ops[s3] = lds_nat<D>(sK0, 32 + l32, 2 * s3 + half);
     // Key tile t in slot T; slot P holds tile t-1 and slot N tile t+1.
     auto iteration = [&](auto t_c, auto p_c, auto n_c, int t) {
       constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      // phase A: 32 MFMAs beside 32 sigmoids per lane
-      fwd_phase<D>(s_nxt, ring<T>(sK0, sK1, sK2), 1, oacc, p1, ring<P>(sV0, sV1, sV2), 1, p0, s_cur, qf, c1, c0,
-                   l32, half, lane);
-      pin_before_barrier(p0);
-      dma_wait();       // this wave's DMA of tile t+1 has landed
-      __syncthreads();  // ... everyone's has, and every wave is done with slot P
-      if (t + 2 < nkt3) fetch(ring<P>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), t + 2);
-      // phase B. At the last tile the new S comes from a stale slot and is never used.
-      fwd_phase<D>(s_cur, ring<N>(sK0, sK1, sK2), 0, oacc, p0, ring<T>(sV0, sV1, sV2), 0, p1, s_nxt, qf, c1, c0,
-                   l32, half, lane);
+      // Tile t+2's DMA into slot P, chunk i (K chunks, then V chunks). Tiles
+      // at or past n_k get no row in range and arrive as zeros.
+      auto dma_chunk = [&](int i) {
+        constexpr int NC = kDmaChunks<D, C::BK, 256>;
+        const int k0 = (t + 2) * C::BK;
+        const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
+        if (i < NC)
+          dma_tile_chunk<D, C::BK, 256>(ring<P>(sK0, sK1, sK2), Kb + off, row_bytes, nk - k0, tid, i);
+        else
+          dma_tile_chunk<D, C::BK, 256>(ring<P>(sV0, sV1, sV2), Vb + off, row_bytes, nk - k0, tid, i - NC);
+      };
+      fwd_tile<D>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2), ring<N>(sK0, sK1, sK2),
+                  s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
+                  [&] {
+                    dma_wait();       // this wave's DMA of tile t+1 has landed
+                    __syncthreads();  // ... everyone's has, and every wave is done with slot P
+                  },
+                  dma_chunk);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -245,6 +299,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
       iteration(I1{}, I0{}, I2{}, t + 1);
       iteration(I2{}, I1{}, I0{}, t + 2);
     }
+    dma_wait();  // the last iterations' DMAs (all zeros) must not outlive the kernel
     // the second half of tile nkt3 - 1 (slot 2)
     accumulate_pv<D>(oacc, p1, sV2, 1, lane);
   }
