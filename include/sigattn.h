@@ -67,6 +67,26 @@ typedef enum {
   SIGATTN_EWORKSPACE = -4     /* workspace smaller than sigattn_workspace_size() */
 } sigattn_status;
 
+/* Where each sample's rows live (sigattn_fwd_ex, sigattn_bwd_ex).
+ *  PADDED: tensors are [Z, L, H, D]; seq_q and seq_k are the lengths n_q[Z] and
+ *          n_k[Z] (the convention of every other entry point).
+ *  PACKED: tensors are [T, H, D], the samples' valid rows back to back with no
+ *          padding; seq_q and seq_k are int32[Z + 1] cumulative offsets (sample
+ *          z owns rows seq[z] .. seq[z+1] - 1, so n = seq[z+1] - seq[z]). L is an
+ *          upper bound on every length: rows of a longer sample past L are
+ *          neither read nor written. Q, O, dO and dQ use seq_q; K, V, dK and dV
+ *          use seq_k. T is implied by the offsets and never passed.
+ * The varlen layout is the packed alternative to padding that the rainbus.top
+ * summary ("局限与改进") and paperlayer.ai (section 3) point to for batches of
+ * very unequal lengths. */
+typedef enum { SIGATTN_LAYOUT_PADDED = 0, SIGATTN_LAYOUT_PACKED = 1 } sigattn_layout;
+
+/* The score bias (paperlayer.ai summary, section 3: b = -log n).
+ *  CONSTANT:   b = bias for every sample.
+ *  NEG_LOG_NK: b_z = bias - ln(n_k[z]) for sample z (ln 1 for n_k = 0). With
+ *              bias = 0 this is the per-sample reading b = -log(n). */
+typedef enum { SIGATTN_BIAS_CONSTANT = 0, SIGATTN_BIAS_NEG_LOG_NK = 1 } sigattn_bias_mode;
+
 /* Which kernel a tile configuration or a counter refers to. */
 typedef enum { SIGATTN_KERNEL_FWD = 0, SIGATTN_KERNEL_DQ = 1, SIGATTN_KERNEL_DKDV = 2 } sigattn_kernel;
 
@@ -142,6 +162,26 @@ int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv,
                    const int32_t* seqlens_q, const int32_t* seqlens_k,
                    int Z, int L, int H, int D, float alpha, float bias, int dtype,
                    int32_t* tile_counts_dkdv, void* stream);
+
+/*
+ * sigattn_fwd and sigattn_bwd with a choice of layout and bias mode (see
+ * sigattn_layout and sigattn_bias_mode). With SIGATTN_LAYOUT_PADDED and
+ * SIGATTN_BIAS_CONSTANT they are exactly sigattn_fwd and sigattn_bwd. In the
+ * packed layout every row of every output belongs to a sample and is written;
+ * tile counters are indexed as in the padded layout, with L tiles per (z, h).
+ * Errors: as sigattn_fwd / sigattn_bwd, plus SIGATTN_EINVAL for an unknown
+ * layout or bias mode. Lengths and offsets live in device memory and are not
+ * checked on the host: offsets must be non-decreasing and within the tensors.
+ */
+int sigattn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
+                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts, void* stream);
+int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout,
+                   void* dq, void* dk, void* dv,
+                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
+                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
 
 /* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
  * backward (any other value) needs for this shape. 0 means none. */

@@ -7,12 +7,17 @@ leg may import this package. The library never does.
 from .sigmoid_attention import (  # noqa: F401
     backward,
     backward_rows,
+    backward_varlen,
     default_scalars,
     forward,
     forward_rows,
+    forward_varlen,
     head_backward,
     head_forward,
+    pack,
+    per_sample_bias,
     scores,
     sigmoid,
     tile_plan,
+    unpack,
 )

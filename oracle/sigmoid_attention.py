@@ -21,7 +21,10 @@ Models" (arXiv:2604.27124):
     transposed view (step 4).
 * gist.science summary, section 2.A: the logistic function
   sigma(x) = 1 / (1 + e^{-x}) and the forward sigma(Q K^T / sqrt(d) + b) V.
-* paperlayer.ai summary, section 3: the bias b = -log(n).
+* paperlayer.ai summary, section 3: the bias b = -log(n), taken either as one
+  scalar for the batch or per sample, b_z = -log(n_k[z]).
+* The packed (varlen) layout: the samples' valid rows back to back, with
+  cumulative offsets, in place of padding (rainbus.top summary, "局限与改进").
 
 Readings taken where the pages are silent (each is listed in the design notes):
 
@@ -116,6 +119,25 @@ def head_backward(qv, kv, vv, dov, alpha, bias, return_intermediates=False):
     return dq, dk, dv
 
 
+def per_sample_bias(seqlens_k, bias=0.0):
+    """b_z = bias - ln(n_k[z]) for every sample z (paperlayer.ai summary,
+    section 3: b = -log n with n the sample's own length). A sample with no
+    key gets bias (ln 1), which no score ever uses."""
+    n = np.asarray(seqlens_k, dtype=np.float64).reshape(-1)
+    return float(bias) - np.log(np.maximum(n, 1.0))
+
+
+def _bias_at(bias, z, Z):
+    """The bias of sample z: bias is one scalar, or an array of Z per-sample values."""
+    b = np.asarray(bias, dtype=np.float64)
+    if b.ndim == 0:
+        return float(b)
+    b = b.reshape(-1)
+    if b.shape[0] != Z:
+        raise ValueError(f"a per-sample bias needs Z={Z} values, got {b.shape[0]}")
+    return float(b[z])
+
+
 def _check_lengths(seqlens, Z, L, name):
     n = np.asarray(seqlens, dtype=np.int64).reshape(-1)
     if n.shape[0] != Z:
@@ -145,7 +167,8 @@ def forward(q, k, v, seqlens_q, seqlens_k, alpha, bias):
 
     Q, K, V are [Z, L, H, D] (rainbus.top summary, "方法步骤详情" step 1).
     For sample z only the prefixes Q[z, :n_q[z]], K[z, :n_k[z]] and
-    V[z, :n_k[z]] are read. Rows i >= n_q[z] of O are 0. Returns float64.
+    V[z, :n_k[z]] are read. Rows i >= n_q[z] of O are 0. bias is one scalar
+    or Z per-sample values (see per_sample_bias). Returns float64.
     """
     Z, L, H, D = _check_qkv(q, k, v)
     nq = _check_lengths(seqlens_q, Z, L, "seqlens_q")
@@ -157,7 +180,7 @@ def forward(q, k, v, seqlens_q, seqlens_k, alpha, bias):
             kv = k[z, :b, h, :]
             vv = v[z, :b, h, :]
             for r0, r1 in _row_blocks(a, b):
-                o[z, r0:r1, h, :] = head_forward(q[z, r0:r1, h, :], kv, vv, alpha, bias)
+                o[z, r0:r1, h, :] = head_forward(q[z, r0:r1, h, :], kv, vv, alpha, _bias_at(bias, z, Z))
     return o
 
 
@@ -182,10 +205,11 @@ def backward(q, k, v, do, seqlens_q, seqlens_k, alpha, bias):
         a, b = int(nq[z]), int(nk[z])
         for h in range(H):
             qv, kv, vv, dov = q[z, :a, h, :], k[z, :b, h, :], v[z, :b, h, :], do[z, :a, h, :]
+            bz = _bias_at(bias, z, Z)
             for r0, r1 in _row_blocks(a, b):
-                dq[z, r0:r1, h, :] = head_backward(qv[r0:r1], kv, vv, dov[r0:r1], alpha, bias)[0]
+                dq[z, r0:r1, h, :] = head_backward(qv[r0:r1], kv, vv, dov[r0:r1], alpha, bz)[0]
             for c0, c1 in _row_blocks(b, a):
-                _, dkb, dvb = head_backward(qv, kv[c0:c1], vv[c0:c1], dov, alpha, bias)
+                _, dkb, dvb = head_backward(qv, kv[c0:c1], vv[c0:c1], dov, alpha, bz)
                 dk[z, c0:c1, h, :] = dkb
                 dv[z, c0:c1, h, :] = dvb
     return dq, dk, dv
@@ -205,7 +229,8 @@ def forward_rows(q, k, v, seqlens_q, seqlens_k, alpha, bias, z, h, rows):
     live = rows < nq[z]
     if live.any():
         b = int(nk[z])
-        out[live] = head_forward(q[z, rows[live], h, :], k[z, :b, h, :], v[z, :b, h, :], alpha, bias)
+        out[live] = head_forward(q[z, rows[live], h, :], k[z, :b, h, :], v[z, :b, h, :], alpha,
+                                 _bias_at(bias, z, Z))
     return out
 
 
@@ -225,12 +250,13 @@ def backward_rows(q, k, v, do, seqlens_q, seqlens_k, alpha, bias, z, h, q_rows, 
     dk = np.zeros((k_rows.shape[0], D), np.float64)
     dv = np.zeros((k_rows.shape[0], D), np.float64)
     qv, kv, vv, dov = q[z, :a, h, :], k[z, :b, h, :], v[z, :b, h, :], do[z, :a, h, :]
+    bz = _bias_at(bias, z, Z)
     lq = q_rows < a
     if lq.any():
-        dq[lq] = head_backward(q[z, q_rows[lq], h, :], kv, vv, do[z, q_rows[lq], h, :], alpha, bias)[0]
+        dq[lq] = head_backward(q[z, q_rows[lq], h, :], kv, vv, do[z, q_rows[lq], h, :], alpha, bz)[0]
     lk = k_rows < b
     if lk.any():
-        _, dkb, dvb = head_backward(qv, k[z, k_rows[lk], h, :], v[z, k_rows[lk], h, :], dov, alpha, bias)
+        _, dkb, dvb = head_backward(qv, k[z, k_rows[lk], h, :], v[z, k_rows[lk], h, :], dov, alpha, bz)
         dk[lk] = dkb
         dv[lk] = dvb
     return dq, dk, dv
@@ -265,6 +291,77 @@ def tile_plan(seqlens_q, seqlens_k, L, block_q, block_k):
                     by_q[z, m] += 1
                     by_k[z, t] += 1
     return by_q, by_k
+
+
+def _check_offsets(cu, name):
+    cu = np.asarray(cu, dtype=np.int64).reshape(-1)
+    if cu.shape[0] < 1 or cu[0] != 0 or (np.diff(cu) < 0).any():
+        raise ValueError(f"{name} must be non-decreasing offsets starting at 0")
+    return cu
+
+
+def pack(x, seqlens):
+    """The packed layout of a padded [Z, L, ...] array: the valid prefixes
+    x[z, :n[z]] back to back, [sum n, ...]. Data movement only."""
+    x = np.asarray(x)
+    n = np.asarray(seqlens, dtype=np.int64).reshape(-1)
+    return np.concatenate([x[z, : int(n[z])] for z in range(x.shape[0])], axis=0)
+
+
+def unpack(xp, cu, L):
+    """The padded layout of a packed array: [Z, L, ...] with sample z's rows
+    cu[z] .. cu[z+1]-1 at positions 0 .. n-1 and zeros after. Data movement only."""
+    xp = np.asarray(xp)
+    cu = _check_offsets(cu, "cu")
+    out = np.zeros((cu.shape[0] - 1, L) + xp.shape[1:], np.float64)
+    for z in range(cu.shape[0] - 1):
+        n = int(cu[z + 1] - cu[z])
+        if n > L:
+            raise ValueError(f"sample {z} has {n} rows, more than L={L}")
+        out[z, :n] = xp[int(cu[z]) : int(cu[z + 1])]
+    return out
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, alpha, bias):
+    """The forward over packed sequences. q is [Tq, H, D] and k, v are
+    [Tk, H, D]. Sample z's queries are rows cu_q[z] .. cu_q[z+1]-1 and its keys
+    rows cu_k[z] .. cu_k[z+1]-1, all valid. Each (z, h) slice is the dense
+    definition. bias is one scalar or Z per-sample values. Returns float64
+    [Tq, H, D]."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    cu_q, cu_k = _check_offsets(cu_q, "cu_q"), _check_offsets(cu_k, "cu_k")
+    Z, H = cu_q.shape[0] - 1, q.shape[1]
+    o = np.zeros(q.shape, np.float64)
+    for z in range(Z):
+        q0, q1, k0, k1 = int(cu_q[z]), int(cu_q[z + 1]), int(cu_k[z]), int(cu_k[z + 1])
+        for h in range(H):
+            for r0, r1 in _row_blocks(q1 - q0, k1 - k0):
+                o[q0 + r0 : q0 + r1, h] = head_forward(q[q0 + r0 : q0 + r1, h], k[k0:k1, h], v[k0:k1, h], alpha,
+                                                        _bias_at(bias, z, Z))
+    return o
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, alpha, bias):
+    """The backward over packed sequences: (dQ [Tq, H, D], dK and dV [Tk, H, D]),
+    float64. Layout and bias as in forward_varlen."""
+    q, k, v, do = np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(do)
+    cu_q, cu_k = _check_offsets(cu_q, "cu_q"), _check_offsets(cu_k, "cu_k")
+    Z, H = cu_q.shape[0] - 1, q.shape[1]
+    dq = np.zeros(q.shape, np.float64)
+    dk = np.zeros(k.shape, np.float64)
+    dv = np.zeros(k.shape, np.float64)
+    for z in range(Z):
+        q0, q1, k0, k1 = int(cu_q[z]), int(cu_q[z + 1]), int(cu_k[z]), int(cu_k[z + 1])
+        bz = _bias_at(bias, z, Z)
+        for h in range(H):
+            qv, kv, vv, dov = q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], do[q0:q1, h]
+            for r0, r1 in _row_blocks(q1 - q0, k1 - k0):
+                dq[q0 + r0 : q0 + r1, h] = head_backward(qv[r0:r1], kv, vv, dov[r0:r1], alpha, bz)[0]
+            for c0, c1 in _row_blocks(k1 - k0, q1 - q0):
+                _, dkb, dvb = head_backward(qv, kv[c0:c1], vv[c0:c1], dov, alpha, bz)
+                dk[k0 + c0 : k0 + c1, h] = dkb
+                dv[k0 + c0 : k0 + c1, h] = dvb
+    return dq, dk, dv
 
 
 def default_scalars(D, L):

@@ -16,6 +16,8 @@ _lib = None
 
 BF16, FP32 = 0, 1
 KERNEL_FWD, KERNEL_DQ, KERNEL_DKDV = 0, 1, 2
+LAYOUT_PADDED, LAYOUT_PACKED = 0, 1
+BIAS_CONSTANT, BIAS_NEG_LOG_NK = 0, 1
 
 EXPORTED_SYMBOLS = (
     "sigattn_fwd",
@@ -24,6 +26,8 @@ EXPORTED_SYMBOLS = (
     "sigattn_bwd_dq",
     "sigattn_bwd_dk",
     "sigattn_bwd_dv",
+    "sigattn_fwd_ex",
+    "sigattn_bwd_ex",
     "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
@@ -62,6 +66,11 @@ def load():
     lib.sigattn_bwd_dk.restype = i32
     lib.sigattn_bwd_dv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
     lib.sigattn_bwd_dv.restype = i32
+    lib.sigattn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, vp]
+    lib.sigattn_fwd_ex.restype = i32
+    lib.sigattn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp,
+                                   vp, vp]
+    lib.sigattn_bwd_ex.restype = i32
     lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

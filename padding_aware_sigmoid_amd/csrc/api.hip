@@ -7,24 +7,25 @@
 #include <cstring>
 
 #include "sigattn.h"
+#include "common.hpp"
 
 namespace sigattn {
 template <int D>
-hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, int, int,
-                           float, float, int32_t*, hipStream_t);
+hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, int32_t*,
+                           hipStream_t);
 template <int D>
-hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, int, int,
-                           float, float, int32_t*, hipStream_t);
-#define SIGATTN_DECL_BWD(NAME)                                                                                   \
-  template <int D>                                                                                               \
-  hipError_t NAME(int, const void*, const void*, const void*, const void*, void*, void*, const int32_t*,        \
-                  const int32_t*, int, int, int, float, float, float, int32_t*, hipStream_t);
+hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, int32_t*,
+                           hipStream_t);
+#define SIGATTN_DECL_BWD(NAME)                                                                                \
+  template <int D>                                                                                            \
+  hipError_t NAME(int, const void*, const void*, const void*, const void*, void*, void*, SeqLayout, int, int, \
+                  float, float, float, int32_t*, hipStream_t);
 SIGATTN_DECL_BWD(launch_dkdv_bf16)
 SIGATTN_DECL_BWD(launch_dkdv_fp32)
-#define SIGATTN_DECL_DQ(NAME)                                                                                    \
-  template <int D>                                                                                               \
-  hipError_t NAME(const void*, const void*, const void*, const void*, void*, const int32_t*, const int32_t*, int, \
-                  int, int, float, float, float, int32_t*, hipStream_t);
+#define SIGATTN_DECL_DQ(NAME)                                                                                 \
+  template <int D>                                                                                            \
+  hipError_t NAME(const void*, const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, \
+                  float, int32_t*, hipStream_t);
 SIGATTN_DECL_DQ(launch_dq_bf16)
 SIGATTN_DECL_DQ(launch_dq_fp32)
 }  // namespace sigattn
@@ -98,33 +99,54 @@ constexpr int kKvBoth = 0, kKvDk = 1, kKvDv = 2;
 namespace {
 
 int launch_dkdv(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                const int32_t* nq, const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                int32_t* tc, hipStream_t st) {
+                sigattn::SeqLayout sl, int Z, int H, int D, float alpha, float bias, int dtype, int32_t* tc,
+                hipStream_t st) {
   const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipError_t e;
   if (dtype == SIGATTN_BF16)
-    e = (D == 64)
-            ? sigattn::launch_dkdv_bf16<64>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-            : sigattn::launch_dkdv_bf16<128>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dkdv_bf16<128>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st);
   else
-    e = (D == 64)
-            ? sigattn::launch_dkdv_fp32<64>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-            : sigattn::launch_dkdv_fp32<128>(mode, q, k, v, dout, dk, dv, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dkdv_fp32<64>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dkdv_fp32<128>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st);
   return hip_status(e);
 }
 
-int launch_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
-              const int32_t* nk, int Z, int L, int H, int D, float alpha, float bias, int dtype, int32_t* tc,
-              hipStream_t st) {
+int launch_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, sigattn::SeqLayout sl, int Z,
+              int H, int D, float alpha, float bias, int dtype, int32_t* tc, hipStream_t st) {
   const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipError_t e;
   if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_dq_bf16<64>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dq_bf16<128>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dq_bf16<64>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dq_bf16<128>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st);
   else
-    e = (D == 64) ? sigattn::launch_dq_fp32<64>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dq_fp32<128>(q, k, v, dout, dq, nq, nk, Z, L, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dq_fp32<64>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dq_fp32<128>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st);
   return hip_status(e);
+}
+
+int launch_fwd(const void* q, const void* k, const void* v, void* o, sigattn::SeqLayout sl, int Z, int H, int D,
+               float alpha, float bias, int dtype, int32_t* tc, hipStream_t st) {
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_fwd_bf16<64>(q, k, v, o, sl, Z, H, c1, c0, tc, st)
+                  : sigattn::launch_fwd_bf16<128>(q, k, v, o, sl, Z, H, c1, c0, tc, st);
+  else
+    e = (D == 64) ? sigattn::launch_fwd_fp32<64>(q, k, v, o, sl, Z, H, c1, c0, tc, st)
+                  : sigattn::launch_fwd_fp32<128>(q, k, v, o, sl, Z, H, c1, c0, tc, st);
+  return hip_status(e);
+}
+
+// The layout of the original entry points: padded [Z, L, H, D], one bias.
+sigattn::SeqLayout padded(const int32_t* nq, const int32_t* nk, int L) { return {nq, nk, L, 0, 0}; }
+
+int check_modes(int layout, int bias_mode) {
+  if (layout != SIGATTN_LAYOUT_PADDED && layout != SIGATTN_LAYOUT_PACKED)
+    return fail(SIGATTN_EINVAL, "unknown layout%s");
+  if (bias_mode != SIGATTN_BIAS_CONSTANT && bias_mode != SIGATTN_BIAS_NEG_LOG_NK)
+    return fail(SIGATTN_EINVAL, "unknown bias mode%s");
+  return 0;
 }
 
 }  // namespace
@@ -136,22 +158,23 @@ int sigattn_fwd(const void* q, const void* k, const void* v, void* o, const int3
                 void* workspace, size_t workspace_bytes, int32_t* tile_counts, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
+  return sigattn_fwd_ex(q, k, v, o, seqlens_q, seqlens_k, SIGATTN_LAYOUT_PADDED, SIGATTN_BIAS_CONSTANT, Z, L, H, D,
+                        alpha, bias, dtype, tile_counts, stream);
+}
+
+int sigattn_fwd_ex(const void* q, const void* k, const void* v, void* o, const int32_t* seq_q, const int32_t* seq_k,
+                   int layout, int bias_mode, int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int32_t* tile_counts, void* stream) {
   g_last_error[0] = '\0';
-  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  int rc = check_modes(layout, bias_mode);
+  if (rc != 0) return rc;
+  rc = check_common(Z, L, H, D, alpha, bias, dtype, seq_q, seq_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(o, "o")))
     return rc;
-  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_fwd_bf16<64>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st)
-                  : sigattn::launch_fwd_bf16<128>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st);
-  else
-    e = (D == 64) ? sigattn::launch_fwd_fp32<64>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st)
-                  : sigattn::launch_fwd_fp32<128>(q, k, v, o, seqlens_q, seqlens_k, Z, L, H, c1, c0, tile_counts, st);
-  return hip_status(e);
+  return launch_fwd(q, k, v, o, {seq_q, seq_k, L, layout, bias_mode}, Z, H, D, alpha, bias, dtype, tile_counts,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
@@ -160,17 +183,29 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, v
                 int32_t* tile_counts_dkdv, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
+  return sigattn_bwd_ex(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, SIGATTN_LAYOUT_PADDED,
+                        SIGATTN_BIAS_CONSTANT, Z, L, H, D, alpha, bias, dtype, tile_counts_dq, tile_counts_dkdv,
+                        stream);
+}
+
+int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode, int Z, int L, int H, int D,
+                   float alpha, float bias, int dtype, int32_t* tile_counts_dq, int32_t* tile_counts_dkdv,
+                   void* stream) {
   g_last_error[0] = '\0';
-  int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
+  int rc = check_modes(layout, bias_mode);
+  if (rc != 0) return rc;
+  rc = check_common(Z, L, H, D, alpha, bias, dtype, seq_q, seq_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) ||
       (rc = check_tensor(dv, "dv")))
     return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  rc = launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dkdv, st);
+  const sigattn::SeqLayout sl{seq_q, seq_k, L, layout, bias_mode};
+  rc = launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, sl, Z, H, D, alpha, bias, dtype, tile_counts_dkdv, st);
   if (rc != SIGATTN_OK) return rc;
-  return launch_dq(q, k, v, dout, dq, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dq, st);
+  return launch_dq(q, k, v, dout, dq, sl, Z, H, D, alpha, bias, dtype, tile_counts_dq, st);
 }
 
 int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
@@ -182,7 +217,7 @@ int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* do
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")))
     return rc;
-  return launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
+  return launch_dkdv(kKvBoth, q, k, v, dout, dk, dv, padded(seqlens_q, seqlens_k, L), Z, H, D, alpha, bias, dtype,
                      tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -195,7 +230,7 @@ int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dk, "dk")))
     return rc;
-  return launch_dkdv(kKvDk, q, k, v, dout, dk, nullptr, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
+  return launch_dkdv(kKvDk, q, k, v, dout, dk, nullptr, padded(seqlens_q, seqlens_k, L), Z, H, D, alpha, bias, dtype,
                      tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -208,8 +243,8 @@ int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv, con
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(dout, "dout")) ||
       (rc = check_tensor(dv, "dv")))
     return rc;
-  return launch_dkdv(kKvDv, q, k, nullptr, dout, nullptr, dv, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype,
-                     tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
+  return launch_dkdv(kKvDv, q, k, nullptr, dout, nullptr, dv, padded(seqlens_q, seqlens_k, L), Z, H, D, alpha, bias,
+                     dtype, tile_counts_dkdv, reinterpret_cast<hipStream_t>(stream));
 }
 
 int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
@@ -221,7 +256,7 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(dout, "dout")) || (rc = check_tensor(dq, "dq")))
     return rc;
-  return launch_dq(q, k, v, dout, dq, seqlens_q, seqlens_k, Z, L, H, D, alpha, bias, dtype, tile_counts_dq,
+  return launch_dq(q, k, v, dout, dq, padded(seqlens_q, seqlens_k, L), Z, H, D, alpha, bias, dtype, tile_counts_dq,
                    reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -253,6 +288,6 @@ const char* sigattn_strerror(int status) {
 
 const char* sigattn_last_error(void) { return g_last_error; }
 
-const char* sigattn_version(void) { return "sigattn-mi355x 0.1 (gfx950)"; }
+const char* sigattn_version(void) { return "sigattn-mi355x 0.2 (gfx950)"; }
 
 }  // extern "C"

@@ -49,9 +49,8 @@ struct BwdCfg {
 template <int D>
 __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                                                      __bf16* __restrict__ dQ, const int32_t* __restrict__ seqlens_q,
-                                                      const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
-                                                      float alpha, float c1, float c0,
+                                                      __bf16* __restrict__ dQ, SeqLayout sl, int Z, int H,
+                                                      float alpha, float c1, float c0_base,
                                                       int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
@@ -61,19 +60,22 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
   __shared__ int rank_lds[kMaxRankedSamples];
-  const int n_qt = (L + C::BQ_DQ - 1) / C::BQ_DQ;
-  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, L, seqlens_q, seqlens_k, rank_lds);
+  const int n_qt = (sl.L + C::BQ_DQ - 1) / C::BQ_DQ;
+  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
   const int z = tcd.z, h = tcd.h, m = tcd.m;
-  const int nq = clamp_len(seqlens_q[z], L);
-  const int nk = clamp_len(seqlens_k[z], L);
+  const int nq = sl.nq(z);
+  const int nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)z * L * H + h) * D;
+  const size_t base = (sl.row0_q(z) * H + h) * D;    // Q, dO and dQ
+  const size_t base_k = (sl.row0_k(z) * H + h) * D;  // K and V
+  const int rows = sl.rows(nq);                       // rows of this sample in dQ
   const int q0 = m * C::BQ_DQ;
   __bf16* dQb = dQ + base;
 
   if (q0 >= nq) {
-    const int rows_here = min(C::BQ_DQ, L - q0);
+    const int rows_here = min(C::BQ_DQ, rows - q0);
     const bf16x8 zz = zero_bf16x8();
     for (int c = tid; c < rows_here * (D / 8); c += 256)
       *(bf16x8*)(dQb + (size_t)(q0 + c / (D / 8)) * rs + (c % (D / 8)) * 8) = zz;
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
   const int nkt3 = (nkt + 2) / 3 * 3;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Kb = K + base;
-    const __bf16* Vb = V + base;
+    const __bf16* Kb = K + base_k;
+    const __bf16* Vb = V + base_k;
     auto fetch = [&](__bf16* sk, __bf16* sv, int tile) {
       const int k0 = tile * C::BK_DQ;
       const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
-        if (row < L) dQb[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? alpha * acc[qb][db][r] : 0.0f);
+        if (row < rows) dQb[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? alpha * acc[qb][db][r] : 0.0f);
       }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
@@ -311,10 +313,8 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                                                        const int32_t* __restrict__ seqlens_q,
-                                                        const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
-                                                        float alpha, float c1, float c0,
-                                                        int32_t* __restrict__ tile_counts) {
+                                                        SeqLayout sl, int Z, int H, float alpha, float c1,
+                                                        float c0_base, int32_t* __restrict__ tile_counts) {
   using C = BwdCfg<D>;
   constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   __shared__ __attribute__((aligned(1024))) __bf16 sQ0[C::TILE];
@@ -324,20 +324,23 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   __shared__ __attribute__((aligned(1024))) __bf16 sG1[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sG2[C::TILE];
   __shared__ int rank_lds[kMaxRankedSamples];
-  const int n_kt = (L + C::BK_KV - 1) / C::BK_KV;
-  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, L, seqlens_q, seqlens_k, rank_lds);
+  const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;
+  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, sl, rank_lds);
   const int z = tcd.z, h = tcd.h, t = tcd.m;
-  const int nq = clamp_len(seqlens_q[z], L);
-  const int nk = clamp_len(seqlens_k[z], L);
+  const int nq = sl.nq(z);
+  const int nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)z * L * H + h) * D;
+  const size_t base = (sl.row0_k(z) * H + h) * D;    // K, V, dK and dV
+  const size_t base_q = (sl.row0_q(z) * H + h) * D;  // Q and dO
+  const int rows = sl.rows(nk);                       // rows of this sample in dK, dV
   const int k0 = t * C::BK_KV;
   __bf16* dKb = dK + base;
   __bf16* dVb = dV + base;
 
   if (k0 >= nk) {
-    const int rows_here = min(C::BK_KV, L - k0);
+    const int rows_here = min(C::BK_KV, rows - k0);
     const bf16x8 zz = zero_bf16x8();
     for (int c = tid; c < rows_here * (D / 8); c += 256) {
       const size_t off = (size_t)(k0 + c / (D / 8)) * rs + (c % (D / 8)) * 8;
@@ -370,8 +373,8 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
   if (nqt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Qb = Q + base;
-    const __bf16* dOb = dO + base;
+    const __bf16* Qb = Q + base_q;
+    const __bf16* dOb = dO + base_q;
     auto fetch = [&](__bf16* sq, __bf16* sg, int tile) {
       const int r0 = tile * C::BQ_KV;
       const size_t off = (size_t)(r0 < nq ? r0 : 0) * rs;  // no row is read past n_q
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = k0 + 64 * w + 32 * kb + acc_row(r, half);
-        if (row < L) {
+        if (row < rows) {
           const bool ok = row < nk;
           if (DO_DK) dKb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? alpha * dkacc[kb][db][r] : 0.0f);
           if (DO_DV) dVb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? dvacc[kb][db][r] : 0.0f);
@@ -457,24 +460,25 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
 template <int D>
 __global__ __launch_bounds__(64) void dq_fp32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, const float* __restrict__ dO,
-                                                     float* __restrict__ dQ, const int32_t* __restrict__ seqlens_q,
-                                                     const int32_t* __restrict__ seqlens_k, int L, int H, float alpha,
-                                                     float c1, float c0, int32_t* __restrict__ tile_counts) {
+                                                     float* __restrict__ dQ, SeqLayout sl, int H, float alpha,
+                                                     float c1, float c0_base, int32_t* __restrict__ tile_counts) {
   constexpr int BQ = 64, BK = 32;
   __shared__ float sK[BK][D];
   __shared__ float sV[BK][D];
   __shared__ float sQr[BQ][D + 1];  // this workgroup's own query rows and dO rows
   __shared__ float sGr[BQ][D + 1];
-  const int n_qt = (L + BQ - 1) / BQ;
+  const int n_qt = (sl.L + BQ - 1) / BQ;
   int bid = blockIdx.x;
   const int m = bid % n_qt;
   bid /= n_qt;
   const int h = bid % H, z = bid / H;
-  const int nq = clamp_len(seqlens_q[z], L), nk = clamp_len(seqlens_k[z], L);
-  const size_t rs = (size_t)H * D, base = ((size_t)z * L * H + h) * D;
+  const int nq = sl.nq(z), nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
+  const size_t rs = (size_t)H * D, base = (sl.row0_q(z) * H + h) * D, base_k = (sl.row0_k(z) * H + h) * D;
+  const int rows = sl.rows(nq);
   const int tid = threadIdx.x, q0 = m * BQ, row = q0 + tid;
   if (q0 >= nq) {
-    if (row < L)
+    if (row < rows)
       for (int d = 0; d < D; ++d) dQ[base + (size_t)row * rs + d] = 0.0f;
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
     return;
@@ -492,8 +496,8 @@ __global__ __launch_bounds__(64) void dq_fp32_kernel(const float* __restrict__ Q
     __syncthreads();
     for (int c = tid; c < BK * D; c += 64) {
       const int r = c / D, d = c % D, kr = t * BK + r;
-      sK[r][d] = kr < nk ? K[base + (size_t)kr * rs + d] : 0.0f;
-      sV[r][d] = kr < nk ? V[base + (size_t)kr * rs + d] : 0.0f;
+      sK[r][d] = kr < nk ? K[base_k + (size_t)kr * rs + d] : 0.0f;
+      sV[r][d] = kr < nk ? V[base_k + (size_t)kr * rs + d] : 0.0f;
     }
     __syncthreads();
     for (int j = 0; j < BK; ++j) {
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(64) void dq_fp32_kernel(const float* __restrict__ Q
       for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(ds, sK[j][d], acc[d]);
     }
   }
-  if (row < L)
+  if (row < rows)
     for (int d = 0; d < D; ++d) dQ[base + (size_t)row * rs + d] = live ? alpha * acc[d] : 0.0f;
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
@@ -516,25 +520,25 @@ template <int D>
 __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        float* __restrict__ dK, float* __restrict__ dV,
-                                                       const int32_t* __restrict__ seqlens_q,
-                                                       const int32_t* __restrict__ seqlens_k, int L, int H,
-                                                       float alpha, float c1, float c0,
+                                                       SeqLayout sl, int H, float alpha, float c1, float c0_base,
                                                        int32_t* __restrict__ tile_counts) {
   constexpr int BK = 64, BQ = 32;
   __shared__ float sQ[BQ][D];
   __shared__ float sdO[BQ][D];
   __shared__ float sKr[BK][D + 1];  // this workgroup's own key rows (+1 pad: conflict-free column walk)
   __shared__ float sVr[BK][D + 1];
-  const int n_kt = (L + BK - 1) / BK;
+  const int n_kt = (sl.L + BK - 1) / BK;
   int bid = blockIdx.x;
   const int t = bid % n_kt;
   bid /= n_kt;
   const int h = bid % H, z = bid / H;
-  const int nq = clamp_len(seqlens_q[z], L), nk = clamp_len(seqlens_k[z], L);
-  const size_t rs = (size_t)H * D, base = ((size_t)z * L * H + h) * D;
+  const int nq = sl.nq(z), nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
+  const size_t rs = (size_t)H * D, base = (sl.row0_k(z) * H + h) * D, base_q = (sl.row0_q(z) * H + h) * D;
+  const int rows = sl.rows(nk);
   const int tid = threadIdx.x, k0 = t * BK, row = k0 + tid;
   if (k0 >= nk) {
-    if (row < L)
+    if (row < rows)
       for (int d = 0; d < D; ++d) {
         if (dK != nullptr) dK[base + (size_t)row * rs + d] = 0.0f;
         if (dV != nullptr) dV[base + (size_t)row * rs + d] = 0.0f;
@@ -556,8 +560,8 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
     __syncthreads();
     for (int c = tid; c < BQ * D; c += 64) {
       const int r = c / D, d = c % D, qr = u * BQ + r;
-      sQ[r][d] = qr < nq ? Q[base + (size_t)qr * rs + d] : 0.0f;
-      sdO[r][d] = qr < nq ? dO[base + (size_t)qr * rs + d] : 0.0f;
+      sQ[r][d] = qr < nq ? Q[base_q + (size_t)qr * rs + d] : 0.0f;
+      sdO[r][d] = qr < nq ? dO[base_q + (size_t)qr * rs + d] : 0.0f;
     }
     __syncthreads();
     for (int i = 0; i < BQ; ++i) {
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
       }
     }
   }
-  if (row < L)
+  if (row < rows)
     for (int d = 0; d < D; ++d) {
       if (dK != nullptr) dK[base + (size_t)row * rs + d] = live ? alpha * dk[d] : 0.0f;
       if (dV != nullptr) dV[base + (size_t)row * rs + d] = live ? dv[d] : 0.0f;
@@ -586,14 +590,13 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
 // MODE: KV_BOTH (dk and dv), KV_DK (dk only) or KV_DV (dv only; v is not read).
 template <int D>
 hipError_t launch_dkdv_bf16(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk,
-                            void* dv, const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha,
-                            float c1, float c0, int32_t* tc, hipStream_t st) {
+                            void* dv, SeqLayout sl, int Z, int H, float alpha, float c1, float c0, int32_t* tc,
+                            hipStream_t st) {
   using C = BwdCfg<D>;
-  const long long blocks = (long long)Z * H * ((L + C::BK_KV - 1) / C::BK_KV);
+  const long long blocks = (long long)Z * H * ((sl.L + C::BK_KV - 1) / C::BK_KV);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, nq, nk, Z, L, H, alpha, c1,
-                       c0, tc);
+                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, sl, Z, H, alpha, c1, c0, tc);
     return hipGetLastError();
   };
   if (mode == KV_DK) return go(dkdv_bf16_kernel<D, KV_DK>);
@@ -606,51 +609,45 @@ hipError_t launch_dkdv_bf16(int mode, const void* q, const void* k, const void* 
 }
 
 template <int D>
-hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
-                          const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0, int32_t* tc,
-                          hipStream_t st) {
+hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dout, void* dq, SeqLayout sl,
+                          int Z, int H, float alpha, float c1, float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
-  const long long blocks = (long long)Z * H * ((L + C::BQ_DQ - 1) / C::BQ_DQ);
+  const long long blocks = (long long)Z * H * ((sl.L + C::BQ_DQ - 1) / C::BQ_DQ);
   hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, nq, nk, Z, L, H, alpha, c1, c0, tc);
+                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, sl, Z, H, alpha, c1, c0, tc);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dkdv_fp32(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk,
-                            void* dv, const int32_t* nq, const int32_t* nk, int Z, int L, int H, float alpha,
-                            float c1, float c0, int32_t* tc, hipStream_t st) {
+                            void* dv, SeqLayout sl, int Z, int H, float alpha, float c1, float c0, int32_t* tc,
+                            hipStream_t st) {
   if (mode == KV_DK) dv = nullptr;
   if (mode == KV_DV) dk = nullptr;
-  const long long blocks = (long long)Z * H * ((L + 63) / 64);
+  const long long blocks = (long long)Z * H * ((sl.L + 63) / 64);
   hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)dout, (float*)dk, (float*)dv, nq, nk, L, H, alpha, c1, c0, tc);
+                     (const float*)v, (const float*)dout, (float*)dk, (float*)dv, sl, H, alpha, c1, c0, tc);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dq_fp32(const void* q, const void* k, const void* v, const void* dout, void* dq, const int32_t* nq,
-                          const int32_t* nk, int Z, int L, int H, float alpha, float c1, float c0, int32_t* tc,
-                          hipStream_t st) {
-  const long long blocks = (long long)Z * H * ((L + 63) / 64);
+hipError_t launch_dq_fp32(const void* q, const void* k, const void* v, const void* dout, void* dq, SeqLayout sl,
+                          int Z, int H, float alpha, float c1, float c0, int32_t* tc, hipStream_t st) {
+  const long long blocks = (long long)Z * H * ((sl.L + 63) / 64);
   hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)dout, (float*)dq, nq, nk, L, H, alpha, c1, c0, tc);
+                     (const float*)v, (const float*)dout, (float*)dq, sl, H, alpha, c1, c0, tc);
   return hipGetLastError();
 }
 
-#define SIGATTN_INST_BWD(D)                                                                                   \
+#define SIGATTN_INST_BWD(D)                                                                                        \
   template hipError_t launch_dkdv_bf16<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
-                                          const int32_t*, const int32_t*, int, int, int, float, float, float,  \
-                                          int32_t*, hipStream_t);                                              \
-  template hipError_t launch_dq_bf16<D>(const void*, const void*, const void*, const void*, void*,              \
-                                        const int32_t*, const int32_t*, int, int, int, float, float, float,    \
-                                        int32_t*, hipStream_t);                                                \
+                                          SeqLayout, int, int, float, float, float, int32_t*, hipStream_t);     \
   template hipError_t launch_dkdv_fp32<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
-                                          const int32_t*, const int32_t*, int, int, int, float, float, float,  \
-                                          int32_t*, hipStream_t);                                              \
-  template hipError_t launch_dq_fp32<D>(const void*, const void*, const void*, const void*, void*,              \
-                                        const int32_t*, const int32_t*, int, int, int, float, float, float,    \
-                                        int32_t*, hipStream_t);
+                                          SeqLayout, int, int, float, float, float, int32_t*, hipStream_t);     \
+  template hipError_t launch_dq_bf16<D>(const void*, const void*, const void*, const void*, void*, SeqLayout,    \
+                                        int, int, float, float, float, int32_t*, hipStream_t);                  \
+  template hipError_t launch_dq_fp32<D>(const void*, const void*, const void*, const void*, void*, SeqLayout,    \
+                                        int, int, float, float, float, int32_t*, hipStream_t);
 SIGATTN_INST_BWD(64)
 SIGATTN_INST_BWD(128)
 

@@ -141,6 +141,40 @@ __device__ __forceinline__ void sched_step() {
 
 __device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
 
+// Where each sample's rows live, how many are valid, and the score bias.
+//  - Padded layout: tensors are [Z, L, H, D]; q and k are the lengths n_q[Z],
+//    n_k[Z]. Sample z owns rows z*L .. z*L + L - 1, and rows at or past its
+//    length are padding (outputs there are written 0).
+//  - Packed layout: tensors are [T, H, D]; q and k are cumulative offsets
+//    cu[Z+1]. Sample z owns rows cu[z] .. cu[z+1] - 1, all valid. L bounds
+//    every length (longer samples are cut at L).
+// Lengths are clamped to [0, L]. With bias_per_sample the bias of sample z is
+// bias - ln(n_k[z]) (paperlayer.ai summary, section 3: b = -log n), which
+// shifts c0 = -b log2(e) by log2(n_k[z]).
+struct SeqLayout {
+  const int32_t* q;
+  const int32_t* k;
+  int L;
+  int packed;
+  int bias_per_sample;
+  __device__ __forceinline__ int len(const int32_t* a, int z) const {
+    return clamp_len(packed ? a[z + 1] - a[z] : a[z], L);
+  }
+  __device__ __forceinline__ int nq(int z) const { return len(q, z); }
+  __device__ __forceinline__ int nk(int z) const { return len(k, z); }
+  // first row of sample z in Q, O, dO, dQ (row0_q) or in K, V, dK, dV (row0_k)
+  __device__ __forceinline__ size_t row0_q(int z) const { return packed ? (size_t)q[z] : (size_t)z * L; }
+  __device__ __forceinline__ size_t row0_k(int z) const { return packed ? (size_t)k[z] : (size_t)z * L; }
+  // rows of sample z present in the tensors, given its clamped length n
+  __device__ __forceinline__ int rows(int n) const { return packed ? n : L; }
+  // The result is uniform; readfirstlane keeps it in a scalar register, as the
+  // constant c0 is, instead of taking a vector register from the kernel.
+  __device__ __forceinline__ float c0_for(float c0, int nk) const {
+    const float c = bias_per_sample ? c0 + __builtin_amdgcn_logf((float)(nk > 1 ? nk : 1)) : c0;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c)));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tile scheduler. A grid covers every (sample z, head h, tile m). Blocks
 // whose tile lies wholly in padding exit at once, so the real work per
@@ -162,9 +196,8 @@ struct TileCoord {
   int z, h, m;
 };
 
-__device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntiles, int L,
-                                                   const int32_t* __restrict__ seqlens_q,
-                                                   const int32_t* __restrict__ seqlens_k, int* rank_lds) {
+__device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntiles, const SeqLayout& sl,
+                                                   int* rank_lds) {
   const int P = Z * H;
   int p, m;
   if ((P & 7) == 0) {
@@ -180,10 +213,10 @@ __device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntil
   if (Z <= kMaxRankedSamples) {
     const int t = threadIdx.x;
     if (t < Z) {
-      const long long wt = (long long)clamp_len(seqlens_q[t], L) * clamp_len(seqlens_k[t], L);
+      const long long wt = (long long)sl.nq(t) * sl.nk(t);
       int rank = 0;
       for (int u = 0; u < Z; ++u) {
-        const long long wu = (long long)clamp_len(seqlens_q[u], L) * clamp_len(seqlens_k[u], L);
+        const long long wu = (long long)sl.nq(u) * sl.nk(u);
         rank += (wu > wt) || (wu == wt && u < t);
       }
       rank_lds[rank] = t;

@@ -189,9 +189,8 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, con
 template <int D>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                                                       const int32_t* __restrict__ seqlens_q,
-                                                       const int32_t* __restrict__ seqlens_k, int Z, int L, int H,
-                                                       float c1, float c0, int32_t* __restrict__ tile_counts) {
+                                                       SeqLayout sl, int Z, int H, float c1, float c0_base,
+                                                       int32_t* __restrict__ tile_counts) {
   using C = FwdCfg<D>;
   static_assert(C::NBUF == 3, "the key loop is unrolled over a ring of three slots");
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
@@ -202,19 +201,22 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
   __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
 
   __shared__ int rank_lds[kMaxRankedSamples];
-  const int n_qt = (L + C::BQ - 1) / C::BQ;
-  const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, L, seqlens_q, seqlens_k, rank_lds);
+  const int n_qt = (sl.L + C::BQ - 1) / C::BQ;
+  const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
   const int z = tc.z, h = tc.h, m = tc.m;
-  const int nq = clamp_len(seqlens_q[z], L);
-  const int nk = clamp_len(seqlens_k[z], L);
+  const int nq = sl.nq(z);
+  const int nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)z * L * H + h) * D;
+  const size_t base = (sl.row0_q(z) * H + h) * D;    // Q and O
+  const size_t base_k = (sl.row0_k(z) * H + h) * D;  // K and V
+  const int rows = sl.rows(nq);                       // rows of this sample in O
   __bf16* Ob = O + base;
   const int q0 = m * C::BQ;
 
   if (q0 >= nq) {  // wholly padded query tile: write zeros, skip all work
-    const int rows_here = min(C::BQ, L - q0);
+    const int rows_here = min(C::BQ, rows - q0);
     const bf16x8 zz = zero_bf16x8();
     for (int c = tid; c < rows_here * (D / 8); c += 256)
       *(bf16x8*)(Ob + (size_t)(q0 + c / (D / 8)) * rs + (c % (D / 8)) * 8) = zz;
@@ -246,8 +248,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
   const int nkt3 = (nkt + 2) / 3 * 3;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Kb = K + base;
-    const __bf16* Vb = V + base;
+    const __bf16* Kb = K + base_k;
+    const __bf16* Vb = V + base_k;
     auto fetch = [&](__bf16* sk, __bf16* sv, int tile) {  // DMA key tile `tile` into one slot
       const int k0 = tile * C::BK;
       const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
-        if (row < L) Ob[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? oacc[qb][db][r] : 0.0f);
+        if (row < rows) Ob[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? oacc[qb][db][r] : 0.0f);
       }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
@@ -323,27 +325,29 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict_
 template <int D>
 __global__ __launch_bounds__(64) void fwd_fp32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
-                                                      const int32_t* __restrict__ seqlens_q,
-                                                      const int32_t* __restrict__ seqlens_k, int L, int H, float c1,
-                                                      float c0, int32_t* __restrict__ tile_counts) {
+                                                      SeqLayout sl, int H, float c1, float c0_base,
+                                                      int32_t* __restrict__ tile_counts) {
   constexpr int BQ = 64, BK = 32;
   __shared__ float sK[BK][D];
   __shared__ float sV[BK][D];
-  const int n_qt = (L + BQ - 1) / BQ;
+  const int n_qt = (sl.L + BQ - 1) / BQ;
   int bid = blockIdx.x;
   const int m = bid % n_qt;
   bid /= n_qt;
   const int h = bid % H;
   const int z = bid / H;
-  const int nq = clamp_len(seqlens_q[z], L);
-  const int nk = clamp_len(seqlens_k[z], L);
+  const int nq = sl.nq(z);
+  const int nk = sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, nk);
   const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)z * L * H + h) * D;
+  const size_t base = (sl.row0_q(z) * H + h) * D;
+  const size_t base_k = (sl.row0_k(z) * H + h) * D;
+  const int rows = sl.rows(nq);
   const int tid = threadIdx.x;
   const int q0 = m * BQ;
   const int row = q0 + tid;
   if (q0 >= nq) {
-    if (row < L)
+    if (row < rows)
       for (int d = 0; d < D; ++d) O[base + (size_t)row * rs + d] = 0.0f;
     if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
     return;
@@ -358,8 +362,8 @@ __global__ __launch_bounds__(64) void fwd_fp32_kernel(const float* __restrict__ 
   for (int t = 0; t < nkt; ++t) {
     for (int c = tid; c < BK * D; c += 64) {
       const int r = c / D, d = c % D, kr = t * BK + r;
-      sK[r][d] = kr < nk ? K[base + (size_t)kr * rs + d] : 0.0f;
-      sV[r][d] = kr < nk ? V[base + (size_t)kr * rs + d] : 0.0f;
+      sK[r][d] = kr < nk ? K[base_k + (size_t)kr * rs + d] : 0.0f;
+      sV[r][d] = kr < nk ? V[base_k + (size_t)kr * rs + d] : 0.0f;
     }
     __syncthreads();
     for (int j = 0; j < BK; ++j) {
@@ -370,38 +374,37 @@ __global__ __launch_bounds__(64) void fwd_fp32_kernel(const float* __restrict__ 
     }
     __syncthreads();
   }
-  if (row < L)
+  if (row < rows)
     for (int d = 0; d < D; ++d) O[base + (size_t)row * rs + d] = live ? o[d] : 0.0f;
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
 }
 
-// Launchers (called from api.cpp). They return the hipError_t of the launch.
+// Launchers (called from api.hip). They return the hipError_t of the launch.
 template <int D>
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, const int32_t* nq, const int32_t* nk,
-                           int Z, int L, int H, float c1, float c0, int32_t* tc, hipStream_t st) {
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, SeqLayout sl, int Z, int H,
+                           float c1, float c0, int32_t* tc, hipStream_t st) {
   using C = FwdCfg<D>;
-  const long long blocks = (long long)Z * H * ((L + C::BQ - 1) / C::BQ);
+  const long long blocks = (long long)Z * H * ((sl.L + C::BQ - 1) / C::BQ);
   hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, nq, nk, Z, L, H, c1, c0, tc);
+                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, sl, Z, H, c1, c0, tc);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, const int32_t* nq, const int32_t* nk,
-                           int Z, int L, int H, float c1, float c0, int32_t* tc, hipStream_t st) {
-  const long long blocks = (long long)Z * H * ((L + 63) / 64);
+hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, SeqLayout sl, int Z, int H,
+                           float c1, float c0, int32_t* tc, hipStream_t st) {
+  const long long blocks = (long long)Z * H * ((sl.L + 63) / 64);
   hipLaunchKernelGGL(fwd_fp32_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, (const float*)q, (const float*)k,
-                     (const float*)v, (float*)o, nq, nk, L, H, c1, c0, tc);
+                     (const float*)v, (float*)o, sl, H, c1, c0, tc);
   return hipGetLastError();
 }
 
-template hipError_t launch_fwd_bf16<64>(const void*, const void*, const void*, void*, const int32_t*, const int32_t*,
-                                        int, int, int, float, float, int32_t*, hipStream_t);
-template hipError_t launch_fwd_bf16<128>(const void*, const void*, const void*, void*, const int32_t*, const int32_t*,
-                                         int, int, int, float, float, int32_t*, hipStream_t);
-template hipError_t launch_fwd_fp32<64>(const void*, const void*, const void*, void*, const int32_t*, const int32_t*,
-                                        int, int, int, float, float, int32_t*, hipStream_t);
-template hipError_t launch_fwd_fp32<128>(const void*, const void*, const void*, void*, const int32_t*, const int32_t*,
-                                         int, int, int, float, float, int32_t*, hipStream_t);
+#define SIGATTN_INST_FWD(NAME, D) \
+  template hipError_t NAME<D>(const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, \
+                              int32_t*, hipStream_t);
+SIGATTN_INST_FWD(launch_fwd_bf16, 64)
+SIGATTN_INST_FWD(launch_fwd_bf16, 128)
+SIGATTN_INST_FWD(launch_fwd_fp32, 64)
+SIGATTN_INST_FWD(launch_fwd_fp32, 128)
 
 }  // namespace sigattn

@@ -54,8 +54,22 @@ def default_alpha(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-def default_bias(L: int) -> float:
-    return -math.log(L)
+def default_bias(L: int, bias_mode: int = _lib.BIAS_CONSTANT) -> float:
+    """-ln L with one bias for every sample; 0 when the bias is per sample
+    (b_z = bias - ln n_k[z])."""
+    return 0.0 if bias_mode == _lib.BIAS_NEG_LOG_NK else -math.log(L)
+
+
+_BIAS_MODES = {"constant": _lib.BIAS_CONSTANT, "neg_log_nk": _lib.BIAS_NEG_LOG_NK}
+
+
+def _bias_mode(mode) -> int:
+    if isinstance(mode, str):
+        try:
+            return _BIAS_MODES[mode]
+        except KeyError:
+            raise ValueError(f"bias_mode must be one of {sorted(_BIAS_MODES)}") from None
+    return int(mode)
 
 
 def _workspace(kernel: int, q: torch.Tensor):
@@ -66,47 +80,138 @@ def _workspace(kernel: int, q: torch.Tensor):
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device), nbytes
 
 
-def sigattn_fwd(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, out=None, tile_counts=None):
-    """O = sigma(alpha q k^T + bias) v with padding. Wraps the C entry point sigattn_fwd.
+def sigattn_fwd(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, out=None, tile_counts=None,
+                bias_mode="constant"):
+    """O = sigma(alpha q k^T + b) v with padding. Wraps the C entry point sigattn_fwd
+    (sigattn_fwd_ex when the bias is per sample).
 
     q, k, v: [Z, L, H, D] bf16 or fp32 on the device. seqlens_*: int32[Z].
-    alpha defaults to 1/sqrt(D) and bias to -log(L).
+    alpha defaults to 1/sqrt(D). bias_mode "constant": b = bias, default -ln L;
+    "neg_log_nk": b_z = bias - ln n_k[z], bias default 0.
     tile_counts, if given, is an int32 device tensor of Z*H*ceil(L/BQ) entries.
     """
     _check_tensors(q, {"k": k, "v": v})
     Z, L, H, D = q.shape
+    mode = _bias_mode(bias_mode)
     alpha = default_alpha(D) if alpha is None else float(alpha)
-    bias = default_bias(L) if bias is None else float(bias)
+    bias = default_bias(L, mode) if bias is None else float(bias)
     nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
     o = torch.empty_like(q) if out is None else out
     _check_tensors(q, {"out": o})
-    ws, wsb = _workspace(_lib.KERNEL_FWD, q)
     lib = _lib.load()
-    _lib.check(lib.sigattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(), nk.data_ptr(),
-                               Z, L, H, D, alpha, bias, _dtype_code(q), None if ws is None else ws.data_ptr(), wsb,
-                               None if tile_counts is None else tile_counts.data_ptr(), _stream(q.device)))
+    tc = None if tile_counts is None else tile_counts.data_ptr()
+    if mode == _lib.BIAS_CONSTANT:
+        ws, wsb = _workspace(_lib.KERNEL_FWD, q)
+        _lib.check(lib.sigattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(),
+                                   nk.data_ptr(), Z, L, H, D, alpha, bias, _dtype_code(q),
+                                   None if ws is None else ws.data_ptr(), wsb, tc, _stream(q.device)))
+    else:
+        _lib.check(lib.sigattn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(),
+                                      nk.data_ptr(), _lib.LAYOUT_PADDED, mode, Z, L, H, D, alpha, bias,
+                                      _dtype_code(q), tc, _stream(q.device)))
     return o
 
 
 def sigattn_bwd(q, k, v, dout, seqlens_q, seqlens_k, alpha=None, bias=None, dq=None, dk=None, dv=None,
-                tile_counts_dq=None, tile_counts_dkdv=None):
-    """(dq, dk, dv) of sigmoid attention. Wraps the C entry point sigattn_bwd."""
+                tile_counts_dq=None, tile_counts_dkdv=None, bias_mode="constant"):
+    """(dq, dk, dv) of sigmoid attention. Wraps the C entry point sigattn_bwd
+    (sigattn_bwd_ex when the bias is per sample). Arguments as for sigattn_fwd."""
     _check_tensors(q, {"k": k, "v": v, "dout": dout})
     Z, L, H, D = q.shape
+    mode = _bias_mode(bias_mode)
     alpha = default_alpha(D) if alpha is None else float(alpha)
-    bias = default_bias(L) if bias is None else float(bias)
+    bias = default_bias(L, mode) if bias is None else float(bias)
     nq, nk = _lengths(seqlens_q, Z, q.device), _lengths(seqlens_k, Z, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     _check_tensors(q, {"dq": dq, "dk": dk, "dv": dv})
-    ws, wsb = _workspace(_lib.KERNEL_DQ, q)
     lib = _lib.load()
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    _lib.check(lib.sigattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                               dk.data_ptr(), dv.data_ptr(), nq.data_ptr(), nk.data_ptr(), Z, L, H, D, alpha, bias,
-                               _dtype_code(q), ptr(ws), wsb, ptr(tile_counts_dq), ptr(tile_counts_dkdv),
-                               _stream(q.device)))
+    if mode == _lib.BIAS_CONSTANT:
+        ws, wsb = _workspace(_lib.KERNEL_DQ, q)
+        _lib.check(lib.sigattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), nq.data_ptr(), nk.data_ptr(), Z, L, H, D, alpha,
+                                   bias, _dtype_code(q), ptr(ws), wsb, ptr(tile_counts_dq), ptr(tile_counts_dkdv),
+                                   _stream(q.device)))
+    else:
+        _lib.check(lib.sigattn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                      dk.data_ptr(), dv.data_ptr(), nq.data_ptr(), nk.data_ptr(), _lib.LAYOUT_PADDED,
+                                      mode, Z, L, H, D, alpha, bias, _dtype_code(q), ptr(tile_counts_dq),
+                                      ptr(tile_counts_dkdv), _stream(q.device)))
+    return dq, dk, dv
+
+
+def _check_packed(q, k, named_q: dict, named_k: dict) -> None:
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed tensors must be [T, H, D]")
+    if q.device.type != "cuda":
+        raise ValueError("sigattn tensors must live on a HIP device")
+    if k.shape[1:] != q.shape[1:] or k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k must match q in H, D, dtype and device")
+    for ref, named in ((q, named_q), (k, named_k)):
+        for name, t in named.items():
+            if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+                raise ValueError(f"{name} must match {'q' if ref is q else 'k'} in shape, dtype and device")
+    for t in (q, k, *named_q.values(), *named_k.values()):
+        if not t.is_contiguous():
+            raise ValueError("packed tensors must be contiguous [T, H, D]")
+
+
+def _offsets(cu, device) -> torch.Tensor:
+    t = cu if isinstance(cu, torch.Tensor) else torch.as_tensor(cu, dtype=torch.int32)
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < 1:
+        raise ValueError("cumulative offsets must be an int32[Z + 1] tensor")
+    return t.to(device).contiguous()
+
+
+def sigattn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None, bias=None, out=None,
+                       tile_counts=None, bias_mode="constant"):
+    """Sigmoid attention over packed sequences. Wraps sigattn_fwd_ex with the packed layout.
+
+    q: [Tq, H, D], k and v: [Tk, H, D]; sample z owns rows cu_seqlens[z] ..
+    cu_seqlens[z+1]-1. max_len bounds every length. alpha defaults to
+    1/sqrt(D); bias as in sigattn_fwd, with L = max_len.
+    """
+    _check_packed(q, k, {}, {"v": v})
+    H, D = q.shape[1], q.shape[2]
+    cq, ck = _offsets(cu_seqlens_q, q.device), _offsets(cu_seqlens_k, q.device)
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
+    Z, L = cq.numel() - 1, int(max_len)
+    mode = _bias_mode(bias_mode)
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(max(L, 1), mode) if bias is None else float(bias)
+    o = torch.empty_like(q) if out is None else out
+    _check_packed(q, k, {"out": o}, {})
+    _lib.check(_lib.load().sigattn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+                                          ck.data_ptr(), _lib.LAYOUT_PACKED, mode, Z, L, H, D, alpha, bias,
+                                          _dtype_code(q), None if tile_counts is None else tile_counts.data_ptr(),
+                                          _stream(q.device)))
+    return o
+
+
+def sigattn_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None, bias=None, dq=None, dk=None,
+                       dv=None, tile_counts_dq=None, tile_counts_dkdv=None, bias_mode="constant"):
+    """(dq, dk, dv) over packed sequences. Wraps sigattn_bwd_ex with the packed layout."""
+    _check_packed(q, k, {"dout": dout}, {"v": v})
+    H, D = q.shape[1], q.shape[2]
+    cq, ck = _offsets(cu_seqlens_q, q.device), _offsets(cu_seqlens_k, q.device)
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
+    Z, L = cq.numel() - 1, int(max_len)
+    mode = _bias_mode(bias_mode)
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(max(L, 1), mode) if bias is None else float(bias)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check_packed(q, k, {"dq": dq}, {"dk": dk, "dv": dv})
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _lib.check(_lib.load().sigattn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                          dk.data_ptr(), dv.data_ptr(), cq.data_ptr(), ck.data_ptr(),
+                                          _lib.LAYOUT_PACKED, mode, Z, L, H, D, alpha, bias, _dtype_code(q),
+                                          ptr(tile_counts_dq), ptr(tile_counts_dkdv), _stream(q.device)))
     return dq, dk, dv
 
 
@@ -189,25 +294,55 @@ class SigmoidAttention(torch.autograd.Function):
     recomputes P and needs neither O nor any row statistic."""
 
     @staticmethod
-    def forward(ctx, q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None):
+    def forward(ctx, q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, bias_mode="constant"):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         Z, L, H, D = q.shape
         nq = _lengths(seqlens_q, Z, q.device)
         nk = _lengths(seqlens_k, Z, q.device)
+        mode = _bias_mode(bias_mode)
         alpha = default_alpha(D) if alpha is None else float(alpha)
-        bias = default_bias(L) if bias is None else float(bias)
+        bias = default_bias(L, mode) if bias is None else float(bias)
         ctx.save_for_backward(q, k, v, nq, nk)
-        ctx.scalars = (alpha, bias)
-        return sigattn_fwd(q, k, v, nq, nk, alpha, bias)
+        ctx.scalars = (alpha, bias, mode)
+        return sigattn_fwd(q, k, v, nq, nk, alpha, bias, bias_mode=mode)
 
     @staticmethod
     def backward(ctx, grad_out):
         q, k, v, nq, nk = ctx.saved_tensors
-        alpha, bias = ctx.scalars
-        dq, dk, dv = sigattn_bwd(q, k, v, grad_out.contiguous(), nq, nk, alpha, bias)
-        return dq, dk, dv, None, None, None, None
+        alpha, bias, mode = ctx.scalars
+        dq, dk, dv = sigattn_bwd(q, k, v, grad_out.contiguous(), nq, nk, alpha, bias, bias_mode=mode)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def sigmoid_attention(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None):
+def sigmoid_attention(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, bias_mode="constant"):
     """Differentiable padding-aware sigmoid attention over [Z, L, H, D] tensors."""
-    return SigmoidAttention.apply(q, k, v, seqlens_q, seqlens_k, alpha, bias)
+    return SigmoidAttention.apply(q, k, v, seqlens_q, seqlens_k, alpha, bias, bias_mode)
+
+
+class SigmoidAttentionVarlen(torch.autograd.Function):
+    """Autograd wrapper over packed [T, H, D] sequences."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None, bias=None, bias_mode="constant"):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        cq, ck = _offsets(cu_seqlens_q, q.device), _offsets(cu_seqlens_k, q.device)
+        mode = _bias_mode(bias_mode)
+        alpha = default_alpha(q.shape[2]) if alpha is None else float(alpha)
+        bias = default_bias(max(int(max_len), 1), mode) if bias is None else float(bias)
+        ctx.save_for_backward(q, k, v, cq, ck)
+        ctx.scalars = (int(max_len), alpha, bias, mode)
+        return sigattn_fwd_varlen(q, k, v, cq, ck, max_len, alpha, bias, bias_mode=mode)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        q, k, v, cq, ck = ctx.saved_tensors
+        max_len, alpha, bias, mode = ctx.scalars
+        dq, dk, dv = sigattn_bwd_varlen(q, k, v, grad_out.contiguous(), cq, ck, max_len, alpha, bias,
+                                        bias_mode=mode)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def sigmoid_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None, bias=None,
+                             bias_mode="constant"):
+    """Differentiable sigmoid attention over packed [T, H, D] sequences."""
+    return SigmoidAttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha, bias, bias_mode)

@@ -387,6 +387,92 @@ def pin_default_scalars():
     assert a == 0.125 and abs(b + math.log(256)) < 1e-15
 
 
+# ------------------------------------------------------------- per-sample bias, packed layout
+def pin_per_sample_bias_closed_form():
+    """With Q = 0 and the per-sample bias b_z = -ln n_k[z] (paperlayer.ai §3,
+    b = -log n), every score of sample z is b_z, so every weight is exactly
+    sigma(-ln n) = 1/(1 + n), taken here from the integers alone. For i < n_q
+    and j < n_k:
+      O_i  = sum_j V_j / (1 + n_k)
+      dV_j = sum_i dO_i / (1 + n_k)
+      dQ_i = alpha n_k / (1 + n_k)^2 * sum_j (dO_i . V_j) K_j
+      dK_j = 0
+    The same holds in the packed layout, sample by sample."""
+    rng = np.random.default_rng(14)
+    Z, L, H, D = 3, 10, 2, 3
+    nq, nk = [10, 4, 7], [6, 10, 1]
+    alpha = 0.9
+    _, k, v, do, nq, nk = _case(rng, Z, L, H, D, nq, nk)
+    q = np.zeros_like(k)
+    bias = osa.per_sample_bias(nk, 0.0)
+    o_w, dq_w, dv_w = (np.zeros((Z, L, H, D)) for _ in range(3))
+    for z in range(Z):
+        a, b = int(nq[z]), int(nk[z])
+        w = 1.0 / (1 + b)
+        for h in range(H):
+            o_w[z, :a, h] = w * v[z, :b, h].sum(0)
+            dv_w[z, :b, h] = w * do[z, :a, h].sum(0)
+            for i in range(a):
+                acc = np.zeros(D)
+                for j in range(b):
+                    acc += float(do[z, i, h] @ v[z, j, h]) * k[z, j, h]
+                dq_w[z, i, h] = alpha * b / (1 + b) ** 2 * acc
+    _close(osa.forward(q, k, v, nq, nk, alpha, bias), o_w, what="O, per-sample bias, Q=0")
+    dq, dk, dv = osa.backward(q, k, v, do, nq, nk, alpha, bias)
+    _close(dq, dq_w, what="dQ, per-sample bias, Q=0")
+    _close(dk, np.zeros_like(dk), what="dK, per-sample bias, Q=0")
+    _close(dv, dv_w, what="dV, per-sample bias, Q=0")
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    cu_k = np.concatenate([[0], np.cumsum(nk)])
+    qp, kp, vp, dop = (np.concatenate([t[z, : int(n[z])] for z in range(Z)]) for t, n in
+                       ((q, nq), (k, nk), (v, nk), (do, nq)))
+    _close(osa.forward_varlen(qp, kp, vp, cu_q, cu_k, alpha, bias),
+           np.concatenate([o_w[z, : int(nq[z])] for z in range(Z)]), what="packed O, per-sample bias, Q=0")
+    dqp, dkp, dvp = osa.backward_varlen(qp, kp, vp, dop, cu_q, cu_k, alpha, bias)
+    _close(dqp, np.concatenate([dq_w[z, : int(nq[z])] for z in range(Z)]), what="packed dQ, Q=0")
+    _close(dkp, np.zeros_like(dkp), what="packed dK, Q=0")
+    _close(dvp, np.concatenate([dv_w[z, : int(nk[z])] for z in range(Z)]), what="packed dV, Q=0")
+
+
+def pin_varlen_matches_padded():
+    """The packed layout is the padded one with the padding removed: on the
+    same valid rows, forward_varlen and backward_varlen (which slice the packed
+    arrays by offsets) equal forward and backward on the padded arrays (which
+    slice by lengths), for one bias and for per-sample biases, with n_q != n_k
+    and an empty sample."""
+    rng = np.random.default_rng(15)
+    Z, L, H, D = 4, 9, 2, 4
+    nq, nk = np.array([9, 3, 0, 5]), np.array([4, 9, 2, 1])
+    q, k, v, do, nq, nk = _case(rng, Z, L, H, D, nq, nk, scale=0.8)
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    cu_k = np.concatenate([[0], np.cumsum(nk)])
+    qp, dop = osa.pack(q, nq), osa.pack(do, nq)
+    kp, vp = osa.pack(k, nk), osa.pack(v, nk)
+    assert qp.shape == (int(nq.sum()), H, D) and kp.shape == (int(nk.sum()), H, D)
+    for bias in (-1.1, osa.per_sample_bias(nk, 0.3)):
+        o = osa.forward(q, k, v, nq, nk, 0.6, bias)
+        _close(osa.forward_varlen(qp, kp, vp, cu_q, cu_k, 0.6, bias), osa.pack(o, nq), what="packed O")
+        dq, dk, dv = osa.backward(q, k, v, do, nq, nk, 0.6, bias)
+        dqp, dkp, dvp = osa.backward_varlen(qp, kp, vp, dop, cu_q, cu_k, 0.6, bias)
+        _close(dqp, osa.pack(dq, nq), what="packed dQ")
+        _close(dkp, osa.pack(dk, nk), what="packed dK")
+        _close(dvp, osa.pack(dv, nk), what="packed dV")
+
+
+def pin_pack_roundtrip():
+    """unpack(pack(x)) keeps the valid prefixes and zeroes the rest."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((3, 5, 2))
+    n = np.array([5, 0, 2])
+    xp = osa.pack(x, n)
+    assert xp.shape == (7, 2)
+    y = osa.unpack(xp, np.concatenate([[0], np.cumsum(n)]), 5)
+    want = x.copy()
+    want[1, :] = 0
+    want[2, 2:] = 0
+    _close(y, want, rtol=0, atol=0, what="pack/unpack")
+
+
 ALL_PINS = [
     pin_sigmoid_closed_forms,
     pin_derivative_bound,
@@ -404,4 +490,7 @@ ALL_PINS = [
     pin_row_sampling,
     pin_tile_plan,
     pin_default_scalars,
+    pin_per_sample_bias_closed_form,
+    pin_varlen_matches_padded,
+    pin_pack_roundtrip,
 ]

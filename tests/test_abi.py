@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_bwd_dk",
-              "sigattn_bwd_dv", "sigattn_tile_config",
+              "sigattn_bwd_dv", "sigattn_fwd_ex", "sigattn_bwd_ex", "sigattn_tile_config",
               "sigattn_workspace_size", "sigattn_strerror", "sigattn_last_error", "sigattn_version"):
         assert n in names
 
@@ -64,6 +64,16 @@ def test_argument_errors_need_no_gpu(lib):
     assert lib.sigattn_bwd_dv(fake0, fake0, fake0, null, fake0, fake0, 1, 8, 1, 128, 1.0, 0.0, 0, null, null) == -1
     assert b"tensor dv is NULL" in lib.sigattn_last_error()
     assert lib.sigattn_bwd_dv(null, null, null, null, null, null, 0, 8, 1, 128, 1.0, 0.0, 0, null, null) == 0
+    # layout and bias mode of the _ex entry points
+    assert lib.sigattn_fwd_ex(null, null, null, null, null, null, 2, 0, 1, 8, 1, 64, 1.0, 0.0, 0, null, null) == -1
+    assert b"layout" in lib.sigattn_last_error()
+    assert lib.sigattn_fwd_ex(null, null, null, null, null, null, 1, 7, 1, 8, 1, 64, 1.0, 0.0, 0, null, null) == -1
+    assert b"bias mode" in lib.sigattn_last_error()
+    assert lib.sigattn_bwd_ex(null, null, null, null, null, null, null, null, null, 1, 1, 1, 8, 1, 96, 1.0, 0.0, 0,
+                              null, null, null) == -1
+    assert b"D must be" in lib.sigattn_last_error()
+    # an empty packed batch is a no-op success
+    assert lib.sigattn_fwd_ex(null, null, null, null, null, null, 1, 1, 0, 8, 1, 64, 1.0, 0.0, 0, null, null) == 0
     # NULL tensors (lengths non-NULL but never dereferenced on the host)
     fake = ctypes.c_void_p(16)
     assert lib.sigattn_fwd(null, null, null, null, fake, fake, 1, 8, 1, 64, 1.0, 0.0, 0, null, 0, null, null) == -1

@@ -20,6 +20,33 @@ _orig_head_backward = osa.head_backward
 _orig_forward = osa.forward
 _orig_backward = osa.backward
 _orig_tile_plan = osa.tile_plan
+_orig_bias_at = osa._bias_at
+_orig_per_sample_bias = osa.per_sample_bias
+_orig_forward_varlen = osa.forward_varlen
+_orig_backward_varlen = osa.backward_varlen
+
+
+def _varlen_fwd(variant):
+    """A packed forward that gets the offsets wrong."""
+
+    def f(q, k, v, cu_q, cu_k, alpha, bias):
+        q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+        cu_q, cu_k = np.asarray(cu_q).astype(int), np.asarray(cu_k).astype(int)
+        o = np.zeros(q.shape)
+        Z = cu_q.shape[0] - 1
+        for z in range(Z):
+            q0, q1, k0, k1 = cu_q[z], cu_q[z + 1], cu_k[z], cu_k[z + 1]
+            if variant == "varlen keys use query offsets":
+                k0, k1 = min(cu_q[z], k.shape[0]), min(cu_q[z + 1], k.shape[0])
+            if variant == "varlen keys shifted by one":
+                k0, k1 = min(k0 + 1, k.shape[0]), min(k1 + 1, k.shape[0])
+            for h in range(q.shape[1]):
+                if q1 > q0:
+                    o[q0:q1, h] = osa.head_forward(q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], alpha,
+                                                   osa._bias_at(bias, z, Z))
+        return o
+
+    return f
 
 
 def _hb(variant):
@@ -129,6 +156,13 @@ MUTANTS = {
     "one padded key read": ("forward", _forward_mask("one padded key read")),
     "padded keys get gradients": ("backward", _backward_mask("padded keys get gradients")),
     "tile plan off by one": ("tile_plan", _tile_plan_off_by_one),
+    "per-sample bias sign": ("per_sample_bias", lambda n, bias=0.0: float(bias) + np.log(np.maximum(
+        np.asarray(n, float).reshape(-1), 1.0))),
+    "per-sample bias log2": ("per_sample_bias", lambda n, bias=0.0: float(bias) - np.log2(np.maximum(
+        np.asarray(n, float).reshape(-1), 1.0))),
+    "bias of the wrong sample": ("_bias_at", lambda bias, z, Z: _orig_bias_at(bias, (z + 1) % Z, Z)),
+    "varlen keys use query offsets": ("forward_varlen", _varlen_fwd("varlen keys use query offsets")),
+    "varlen keys shifted by one": ("forward_varlen", _varlen_fwd("varlen keys shifted by one")),
 }
 
 
