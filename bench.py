@@ -16,6 +16,8 @@ Definitions:
   dominant kernel.
 * The line also carries the 25%-padding workload at the same shape per
   sample. The pages report both no padding and 25% padding.
+* `varlen`: the cell-batch workload (71% padded tokens) timed fwd+bwd in the
+  padded layout and in the packed layout on the same valid rows.
 
 One GPU only. --gpus above 1 exits with a message.
 """
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="nopad16k")
     ap.add_argument("--pad-workload", default="pad25_16k", help="secondary workload reported in the same line ('' to skip)")
+    ap.add_argument("--varlen-workload", default="cellbatch8k",
+                    help="workload timed in the padded and the packed layout ('none' skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many bytes twice (a plain device copy of "
@@ -125,6 +129,64 @@ def run_gpu(name, steps, warmup, seed=0):
     del q, k, v, do, o, dq, dk, dv
     torch.cuda.empty_cache()
     return res
+
+
+def run_layouts(name, steps, warmup, seed=0):
+    """fwd+bwd of one workload in the padded layout and in the packed (varlen)
+    layout, on the same valid rows, each timed with HIP events on the launch
+    stream over `steps` steps. Returns ms per step for both."""
+    import numpy as np
+    import torch
+
+    import padding_aware_sigmoid_amd as sa
+    import workloads
+    from padding_aware_sigmoid_amd import accounting
+
+    inp = workloads.make_inputs(name, seed=seed)
+    w = inp["workload"]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    n = inp["seqlens_q"]
+    nq = torch.as_tensor(n).to(dev)
+    nk = torch.as_tensor(inp["seqlens_k"]).to(dev)
+    pack = lambda t: torch.cat([t[z, : int(n[z])] for z in range(w.Z)], 0).contiguous()  # noqa: E731
+    qp, kp, vp, dop = (pack(t) for t in (q, k, v, do))
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32)).to(dev)
+    a, b = w.alpha, w.bias
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    op, dqp, dkp, dvp = (torch.empty_like(qp) for _ in range(4))
+    stream = torch.cuda.current_stream(dev)
+
+    def padded():
+        sa.sigattn_fwd(q, k, v, nq, nk, a, b, out=o)
+        sa.sigattn_bwd(q, k, v, do, nq, nk, a, b, dq=dq, dk=dk, dv=dv)
+
+    def packed():
+        sa.sigattn_fwd_varlen(qp, kp, vp, cu, cu, w.L, a, b, out=op)
+        sa.sigattn_bwd_varlen(qp, kp, vp, dop, cu, cu, w.L, a, b, dq=dqp, dk=dkp, dv=dvp)
+
+    res = {}
+    for label, fn in (("padded", padded), ("packed", packed)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[label] = e0.elapsed_time(e1) / steps
+    fl = accounting.attention_flops(w.Z, w.L, w.H, w.D, inp["seqlens_q"], inp["seqlens_k"])
+    out = {"workload": w.name, "Z": w.Z, "H": w.H, "L": w.L, "D": w.D, "lengths": n.tolist(),
+           "valid_token_fraction": round(float(n.sum()) / (w.Z * w.L), 4)}
+    for label, ms in res.items():
+        out[f"{label}_ms"] = round(ms, 4)
+        out[f"{label}_tflops_valid"] = round(fl["total_valid"] / (ms * 1e-3) / 1e12, 2)
+    out["packed_speedup"] = round(res["padded"] / res["packed"], 3)
+    del q, k, v, do, qp, kp, vp, dop, o, dq, dk, dv, op, dqp, dkp, dvp
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(name, heads=2):
@@ -228,6 +290,8 @@ def main():
             "bwd_tflops_valid": round(pad_res["bwd_tflops_valid"], 2),
             "tflops_loss_vs_nopad": round(1.0 - pad_res["tflops_valid"] / main_res["tflops_valid"], 4),
         }
+    if args.varlen_workload not in ("", "none"):
+        line["varlen"] = run_layouts(args.varlen_workload, args.steps, args.warmup)
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)

@@ -40,6 +40,8 @@ def kernel_source_hash() -> str:
 def short_name(kernel: str) -> str | None:
     """The bench name of a sigattn kernel from its demangled name, else None."""
     m = re.search(r"sigattn::(fwd|dq|dkdv)_(bf16|fp32)_kernel<(\d+)(?:,\s*(\d))?>", kernel)
+    if m is None:  # the mangled form, e.g. _ZN7sigattn16dkdv_bf16_kernelILi128ELi2EEEv...
+        m = re.search(r"_ZN7sigattn\d+(fwd|dq|dkdv)_(bf16|fp32)_kernelILi(\d+)E(?:Li(\d)E)?", kernel)
     if m is None:
         return None
     kind, dtype, _, mode = m.groups()
