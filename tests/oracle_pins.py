@@ -21,6 +21,7 @@ import pathlib
 import numpy as np
 
 from oracle import sigmoid_attention as osa
+from oracle import softmax_attention as sma
 
 GOLDEN = pathlib.Path(__file__).parent / "golden"
 
@@ -473,6 +474,153 @@ def pin_pack_roundtrip():
     _close(y, want, rtol=0, atol=0, what="pack/unpack")
 
 
+# ------------------------------------------------------------------------------ softmax path
+def pin_softmax_q_zero_closed_form():
+    """With Q = 0 every score of a row is 0, so every weight is exactly 1/n_k
+    (rainbus.top summary, 前置知识, "Softmax 归一化": e^0 / sum e^0). For
+    i < n_q, j < n_k:
+      O_i = sum_j V_j / n_k,  LSE_i = ln n_k,
+      dV_j = sum_i dO_i / n_k,  dK_j = 0,
+      dQ_i = alpha / n_k * sum_j (dO_i . V_j - dO_i . O_i) K_j."""
+    rng = np.random.default_rng(30)
+    Z, L, H, D = 2, 11, 2, 3
+    nq, nk = [11, 5], [7, 11]
+    alpha = 0.8
+    _, k, v, do, nq, nk = _case(rng, Z, L, H, D, nq, nk)
+    q = np.zeros_like(k)
+    o_w, dq_w, dv_w = (np.zeros((Z, L, H, D)) for _ in range(3))
+    lse_w = np.zeros((Z, H, L))
+    for z in range(Z):
+        a, b = int(nq[z]), int(nk[z])
+        for h in range(H):
+            mean_v = v[z, :b, h].sum(0) / b
+            o_w[z, :a, h] = mean_v
+            lse_w[z, h, :a] = math.log(b)
+            dv_w[z, :b, h] = do[z, :a, h].sum(0) / b
+            for i in range(a):
+                acc = np.zeros(D)
+                for j in range(b):
+                    acc += (float(do[z, i, h] @ v[z, j, h]) - float(do[z, i, h] @ mean_v)) * k[z, j, h]
+                dq_w[z, i, h] = alpha / b * acc
+    o, lse = sma.forward(q, k, v, nq, nk, alpha)
+    _close(o, o_w, what="softmax O with Q=0")
+    _close(lse, lse_w, what="softmax LSE with Q=0")
+    dq, dk, dv = sma.backward(q, k, v, do, nq, nk, alpha)
+    _close(dq, dq_w, what="softmax dQ with Q=0")
+    _close(dk, np.zeros_like(dk), what="softmax dK with Q=0")
+    _close(dv, dv_w, what="softmax dV with Q=0")
+
+
+def _torch_softmax_reference(q, k, v, do, nq, nk, alpha):
+    import torch
+
+    Z, L, H, D = q.shape
+    outs = [np.zeros((Z, L, H, D)) for _ in range(4)]
+    lse = np.zeros((Z, H, L))
+    for z in range(Z):
+        a, b = int(nq[z]), int(nk[z])
+        if a == 0 or b == 0:
+            continue
+        for h in range(H):
+            tq, tk, tv = (torch.tensor(t[z, :, h], dtype=torch.float64, requires_grad=True) for t in (q, k, v))
+            s = alpha * tq @ tk.T
+            s = s.masked_fill(torch.arange(L)[None, :] >= b, float("-inf"))
+            w = torch.softmax(s, dim=1)
+            o = w @ tv
+            o = o.masked_fill(torch.arange(L)[:, None] >= a, 0.0)
+            (o * torch.tensor(do[z, :, h])).sum().backward()
+            outs[0][z, :, h] = o.detach().numpy()
+            outs[1][z, :, h] = tq.grad.numpy()
+            outs[2][z, :, h] = tk.grad.numpy()
+            outs[3][z, :, h] = tv.grad.numpy()
+            lse[z, h, :a] = torch.logsumexp(s, dim=1).detach().numpy()[:a]
+    return outs, lse
+
+
+def pin_softmax_torch():
+    """Dense torch.softmax / logsumexp / autograd in float64, padded keys masked
+    with -inf and padded query rows zeroed, against the oracle's forward and
+    backward (which take dK/dV through the row statistics)."""
+    rng = np.random.default_rng(31)
+    Z, L, H, D = 3, 13, 2, 4
+    q, k, v, do, nq, nk = _case(rng, Z, L, H, D, [13, 6, 9], [9, 13, 1], scale=1.5)
+    (o_t, dq_t, dk_t, dv_t), lse_t = _torch_softmax_reference(q, k, v, do, nq, nk, 0.7)
+    o, lse = sma.forward(q, k, v, nq, nk, 0.7)
+    _close(o, o_t, rtol=1e-10, atol=1e-12, what="softmax O vs torch")
+    _close(lse, lse_t, rtol=1e-10, atol=1e-12, what="softmax LSE vs torch")
+    dq, dk, dv = sma.backward(q, k, v, do, nq, nk, 0.7)
+    _close(dq, dq_t, rtol=1e-10, atol=1e-12, what="softmax dQ vs torch")
+    _close(dk, dk_t, rtol=1e-10, atol=1e-12, what="softmax dK vs torch")
+    _close(dv, dv_t, rtol=1e-10, atol=1e-12, what="softmax dV vs torch")
+
+
+def pin_softmax_small_blocks():
+    """The backward again, with blocks of a few rows: the key-block route
+    (P = e^{S - LSE}, D = dO . O) must not renormalise inside a block."""
+    from oracle import sigmoid_attention as base
+
+    rng = np.random.default_rng(32)
+    q, k, v, do, nq, nk = _case(rng, 2, 12, 1, 3, [12, 5], [12, 9], scale=2.0)
+    (_, dq_t, dk_t, dv_t), _ = _torch_softmax_reference(q, k, v, do, nq, nk, 0.9)
+    saved = base._MAX_BLOCK_ELEMS
+    base._MAX_BLOCK_ELEMS = 30  # blocks of 2-3 rows
+    try:
+        dq, dk, dv = sma.backward(q, k, v, do, nq, nk, 0.9)
+        o_r, lse_r = sma.forward_rows(q, k, v, nq, nk, 0.9, 0, 0, np.arange(12))
+        bq, bk, bv = sma.backward_rows(q, k, v, do, nq, nk, 0.9, 1, 0, np.arange(12), np.arange(12))
+    finally:
+        base._MAX_BLOCK_ELEMS = saved
+    for n, a, b in (("dQ", dq, dq_t), ("dK", dk, dk_t), ("dV", dv, dv_t)):
+        _close(a, b, rtol=1e-10, atol=1e-12, what=f"softmax {n}, small blocks")
+    o, lse = sma.forward(q, k, v, nq, nk, 0.9)
+    _close(o_r, o[0, :, 0], what="softmax forward_rows")
+    _close(lse_r, lse[0, 0], what="softmax forward_rows LSE")
+    _close(bq, dq_t[1, :, 0], rtol=1e-10, atol=1e-12, what="softmax backward_rows dQ")
+    _close(bk, dk_t[1, :, 0], rtol=1e-10, atol=1e-12, what="softmax backward_rows dK")
+    _close(bv, dv_t[1, :, 0], rtol=1e-10, atol=1e-12, what="softmax backward_rows dV")
+
+
+def pin_softmax_invariants():
+    """Each valid row's weights sum to 1 (V = 1 gives O = 1); a row with no
+    key gives 0; huge scores do not overflow, and a key that leads every other
+    by far takes all the weight."""
+    rng = np.random.default_rng(33)
+    Z, L, H, D = 2, 9, 1, 3
+    q, k, _, do, nq, nk = _case(rng, Z, L, H, D, [9, 4], [6, 0], scale=3.0)
+    ones = np.ones((Z, L, H, D))
+    o, lse = sma.forward(q, k, ones, nq, nk, 1.0)
+    _close(o[0, :9], np.ones((9, H, D)), what="softmax rows sum to 1")
+    assert np.all(o[1] == 0) and np.all(lse[1] == 0), "a row with no key must give 0"
+    # one dominating key: scores 0 except key 3 at 1000
+    q1 = np.zeros((1, 5, 1, 2)); q1[0, :, 0, 0] = 1.0
+    k1 = np.zeros((1, 5, 1, 2)); k1[0, 3, 0, 0] = 1000.0
+    v1 = rng.standard_normal((1, 5, 1, 2))
+    o1, lse1 = sma.forward(q1, k1, v1, [5], [5], 1.0)
+    assert np.all(np.isfinite(o1)) and np.all(np.isfinite(lse1)), "softmax overflowed"
+    _close(o1[0, :, 0], np.repeat(v1[0, 3:4, 0], 5, axis=0), rtol=0, atol=1e-12, what="dominating key")
+    _close(lse1[0, 0], np.full(5, 1000.0), rtol=1e-15, atol=1e-12, what="LSE of a dominating key")
+    dq, dk, dv = sma.backward(q1 * 50, k1, v1, rng.standard_normal((1, 5, 1, 2)), [5], [5], 1.0)
+    assert all(np.all(np.isfinite(t)) for t in (dq, dk, dv)), "softmax gradients overflowed"
+
+
+def pin_softmax_finite_differences():
+    """dQ, dK and dV against central differences of sum(O * G), entry by entry."""
+    rng = np.random.default_rng(34)
+    q, k, v, g, nq, nk = _case(rng, 1, 5, 1, 2, [4], [5])
+    alpha, eps = 0.6, 1e-6
+    dq, dk, dv = sma.backward(q, k, v, g, nq, nk, alpha)
+    loss = lambda qq, kk, vv: float((sma.forward(qq, kk, vv, nq, nk, alpha)[0] * g).sum())  # noqa: E731
+    for name, t, grad in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += eps
+            tm[idx] -= eps
+            args_p = {"dQ": (tp, k, v), "dK": (q, tp, v), "dV": (q, k, tp)}[name]
+            args_m = {"dQ": (tm, k, v), "dK": (q, tm, v), "dV": (q, k, tm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-7, f"softmax {name}{idx}: fd {fd} vs {grad[idx]}"
+
+
 ALL_PINS = [
     pin_sigmoid_closed_forms,
     pin_derivative_bound,
@@ -493,4 +641,9 @@ ALL_PINS = [
     pin_per_sample_bias_closed_form,
     pin_varlen_matches_padded,
     pin_pack_roundtrip,
+    pin_softmax_q_zero_closed_form,
+    pin_softmax_torch,
+    pin_softmax_small_blocks,
+    pin_softmax_invariants,
+    pin_softmax_finite_differences,
 ]

@@ -13,6 +13,7 @@ import pytest
 
 import oracle_pins
 from oracle import sigmoid_attention as osa
+from oracle import softmax_attention as sma
 
 _orig_scores = osa.scores
 _orig_sigmoid = osa.sigmoid
@@ -24,6 +25,49 @@ _orig_bias_at = osa._bias_at
 _orig_per_sample_bias = osa.per_sample_bias
 _orig_forward_varlen = osa.forward_varlen
 _orig_backward_varlen = osa.backward_varlen
+_orig_sm_head_forward = sma.head_forward
+_orig_sm_dkdv = sma._dkdv_by_key_blocks
+
+
+def _sm_forward(variant):
+    def f(qv, kv, vv, alpha):
+        qv, kv, vv = (np.asarray(t, np.float64) for t in (qv, kv, vv))
+        if kv.shape[0] == 0:
+            return np.zeros((qv.shape[0], vv.shape[1])), np.zeros(qv.shape[0])
+        s = alpha * (qv @ kv.T)
+        if variant == "softmax over queries":
+            m = s.max(axis=0, keepdims=True)
+            e = np.exp(s - m)
+            p = e / e.sum(axis=0, keepdims=True)
+            return p @ vv, (m.max() + np.log(e.sum(axis=1)))
+        m = s.max(axis=1, keepdims=True) if variant != "softmax without max" else 0.0
+        e = np.exp(s - m)
+        den = e.sum(axis=1, keepdims=True)
+        lse = np.log(den)[:, 0] if variant == "LSE without max" else (m + np.log(den))[:, 0]
+        return (e / den) @ vv, lse
+
+    return f
+
+
+def _sm_dkdv(variant):
+    def f(qv, kv, vv, dov, alpha, lse, dvec):
+        a, b = qv.shape[0], kv.shape[0]
+        dk = np.zeros(kv.shape)
+        dv = np.zeros(vv.shape)
+        for c0, c1 in osa._row_blocks(b, a):
+            s = alpha * (qv @ kv[c0:c1].T)
+            if variant == "key blocks renormalised":
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+            else:
+                p = np.exp(s - lse[:, None])
+            dp = dov @ vv[c0:c1].T
+            ds = p * dp if variant == "dS drops D" else p * (dp - dvec[:, None])
+            dk[c0:c1] = alpha * (ds.T @ qv)
+            dv[c0:c1] = p.T @ dov
+        return dk, dv
+
+    return f
 
 
 def _varlen_fwd(variant):
@@ -163,13 +207,21 @@ MUTANTS = {
     "bias of the wrong sample": ("_bias_at", lambda bias, z, Z: _orig_bias_at(bias, (z + 1) % Z, Z)),
     "varlen keys use query offsets": ("forward_varlen", _varlen_fwd("varlen keys use query offsets")),
     "varlen keys shifted by one": ("forward_varlen", _varlen_fwd("varlen keys shifted by one")),
+    "softmax over queries": ("sm:head_forward", _sm_forward("softmax over queries")),
+    "softmax without max": ("sm:head_forward", _sm_forward("softmax without max")),
+    "LSE without max": ("sm:head_forward", _sm_forward("LSE without max")),
+    "key blocks renormalised": ("sm:_dkdv_by_key_blocks", _sm_dkdv("key blocks renormalised")),
+    "dS drops D": ("sm:_dkdv_by_key_blocks", _sm_dkdv("dS drops D")),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(osa, attr, fn)
+    module = osa
+    if attr.startswith("sm:"):
+        module, attr = sma, attr[3:]
+    monkeypatch.setattr(module, attr, fn)
     caught = []
     for pin in oracle_pins.ALL_PINS:
         try:
