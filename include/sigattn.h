@@ -183,6 +183,49 @@ int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout
                    int Z, int L, int H, int D, float alpha, float bias, int dtype,
                    int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
 
+/*
+ * Padding-aware, non-causal SOFTMAX attention, the same padding design applied
+ * to softmax (rainbus.top summary, "未来方向"; the softmax itself is the one
+ * of the "前置知识" entries on self-attention and softmax normalisation):
+ *   S = alpha * Q K^T over the keys j < n_k[z],
+ *   P_ij = e^{S_ij} / sum_{j < n_k} e^{S_ij},  O = P V,
+ *   LSE_i = log sum_{j < n_k} e^{S_ij}  (natural log).
+ * A constant score bias cancels in the row normalisation, so there is no bias.
+ * A row with no valid key (n_k[z] = 0) and every padded row (i >= n_q[z]) get
+ * O = 0 and LSE = 0.
+ * Backward, with P recomputed as e^{S - LSE}:
+ *   dP = dO V^T,  Dvec_i = sum_d dO_id O_id,  dS = P (dP - Dvec),
+ *   dQ = alpha dS K,  dK = alpha dS^T Q,  dV = P^T dO.
+ *
+ * Layout: `layout` as in sigattn_fwd_ex (PADDED with lengths, PACKED with
+ * offsets). lse is fp32 [Z, L, H] (padded) or [T, H] (packed), one value per
+ * query row and head, device memory owned by the caller. O, dO, dQ, dK and dV
+ * follow Q, K and V in dtype and layout. alpha must be > 0: the kernels take
+ * each row's running maximum of alpha q.k to keep e^x finite.
+ * bf16: both contractions run on bf16 MFMA with fp32 accumulation; P and dS
+ * are rounded to bf16 before an MFMA; the running maximum, the row sums and
+ * LSE are fp32. fp32: fp32 throughout.
+ *
+ * sigattn_softmax_bwd takes the forward's O and lse unchanged, and a device
+ * workspace of at least sigattn_softmax_bwd_workspace_size(rows_q, H) bytes,
+ * rows_q being the number of query rows (Z * L padded, T packed). It holds
+ * {LSE log2 e, Dvec} per query row and head between the backward's kernels,
+ * and is written before it is read, so it need not be cleared. The padded
+ * layout's size is checked; the packed layout's T lives in device memory and
+ * is the caller's to respect.
+ * Errors: as sigattn_fwd_ex, plus SIGATTN_EINVAL for alpha <= 0 or a NULL
+ * lse or workspace, and SIGATTN_EWORKSPACE for a workspace that is too small.
+ */
+int sigattn_softmax_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* seq_q, const int32_t* seq_k, int layout,
+                        int Z, int L, int H, int D, float alpha, int dtype, void* stream);
+size_t sigattn_softmax_bwd_workspace_size(long long rows_q, int H);
+int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const int32_t* seq_q, const int32_t* seq_k, int layout,
+                        int Z, int L, int H, int D, float alpha, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
  * backward (any other value) needs for this shape. 0 means none. */
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype);

@@ -1,4 +1,5 @@
-"""Padding-aware, non-causal sigmoid attention for AMD Instinct MI355X (gfx950).
+"""Padding-aware, non-causal sigmoid attention for AMD Instinct MI355X (gfx950),
+and softmax attention with the same padding design.
 
 The compute lives in libsigattn.so: hand-written HIP kernels behind the C ABI
 in include/sigattn.h. This package is its Python binding.
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     SigmoidAttention,
     SigmoidAttentionVarlen,
+    SoftmaxAttention,
     sigattn_bwd,
     sigattn_bwd_dk,
     sigattn_bwd_dkdv,
@@ -30,8 +32,11 @@ from .ops import (  # noqa: F401
     sigattn_bwd_varlen,
     sigattn_fwd,
     sigattn_fwd_varlen,
+    sigattn_softmax_bwd,
+    sigattn_softmax_fwd,
     sigattn_tile_config,
     sigmoid_attention,
     sigmoid_attention_varlen,
+    softmax_attention,
 )
 from .accounting import attention_flops  # noqa: F401

@@ -28,6 +28,9 @@ EXPORTED_SYMBOLS = (
     "sigattn_bwd_dv",
     "sigattn_fwd_ex",
     "sigattn_bwd_ex",
+    "sigattn_softmax_fwd",
+    "sigattn_softmax_bwd",
+    "sigattn_softmax_bwd_workspace_size",
     "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
@@ -71,6 +74,13 @@ def load():
     lib.sigattn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp,
                                    vp, vp]
     lib.sigattn_bwd_ex.restype = i32
+    lib.sigattn_softmax_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.sigattn_softmax_fwd.restype = i32
+    lib.sigattn_softmax_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                        i32, vp, sz, vp]
+    lib.sigattn_softmax_bwd.restype = i32
+    lib.sigattn_softmax_bwd_workspace_size.argtypes = [ctypes.c_longlong, i32]
+    lib.sigattn_softmax_bwd_workspace_size.restype = sz
     lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

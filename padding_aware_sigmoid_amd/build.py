@@ -17,7 +17,9 @@ PKG = pathlib.Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"
 LIB = PKG / "libsigattn.so"
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "bwd_softmax_dk128.hip", "softmax.hip"]
+# Sources built without the VGPR form of MFMA results (see the file's header).
+AGPR_FORM_SOURCES = {"bwd_softmax_dk128.hip"}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -26,11 +28,11 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results go to VGPRs where they fit. The sigma code then reads the
-    # scores without a v_accvgpr_read per value.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
 ]
+# MFMA results go to VGPRs where they fit. The sigma code then reads the scores
+# without a v_accvgpr_read per value. Every source but AGPR_FORM_SOURCES.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:
@@ -57,7 +59,8 @@ def build(verbose: bool = False) -> pathlib.Path:
     jobs = []
     for src in SOURCES:
         obj = objdir / (pathlib.Path(src).stem + ".o")
-        jobs.append((obj, [cc, *COMMON_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]))
+        flags = COMMON_FLAGS + ([] if src in AGPR_FORM_SOURCES else VGPR_FORM)
+        jobs.append((obj, [cc, *flags, "-c", str(CSRC / src), "-o", str(obj)]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):
             if verbose and out.strip():

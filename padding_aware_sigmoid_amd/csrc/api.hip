@@ -16,18 +16,30 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, SeqLayo
 template <int D>
 hipError_t launch_fwd_fp32(const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, int32_t*,
                            hipStream_t);
-#define SIGATTN_DECL_BWD(NAME)                                                                                \
-  template <int D>                                                                                            \
-  hipError_t NAME(int, const void*, const void*, const void*, const void*, void*, void*, SeqLayout, int, int, \
-                  float, float, float, int32_t*, hipStream_t);
-SIGATTN_DECL_BWD(launch_dkdv_bf16)
-SIGATTN_DECL_BWD(launch_dkdv_fp32)
-#define SIGATTN_DECL_DQ(NAME)                                                                                 \
-  template <int D>                                                                                            \
-  hipError_t NAME(const void*, const void*, const void*, const void*, void*, SeqLayout, int, int, float, float, \
-                  float, int32_t*, hipStream_t);
-SIGATTN_DECL_DQ(launch_dq_bf16)
-SIGATTN_DECL_DQ(launch_dq_fp32)
+template <int D>
+hipError_t launch_dkdv_bf16(int, int, const void*, const void*, const void*, const void*, void*, void*, const void*,
+                            SeqLayout, int, int, float, float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_dkdv_fp32(int, const void*, const void*, const void*, const void*, void*, void*, SeqLayout, int, int,
+                            float, float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_dq_bf16(int, const void*, const void*, const void*, const void*, void*, const void*, SeqLayout, int,
+                          int, float, float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_dq_fp32(const void*, const void*, const void*, const void*, void*, SeqLayout, int, int, float,
+                          float, float, int32_t*, hipStream_t);
+template <int D>
+hipError_t launch_sm_fwd_bf16(const void*, const void*, const void*, void*, float*, SeqLayout, int, int, float,
+                              hipStream_t);
+template <int D>
+hipError_t launch_sm_fwd_fp32(const void*, const void*, const void*, void*, float*, SeqLayout, int, int, float,
+                              hipStream_t);
+template <int D>
+hipError_t launch_sm_rowstats(int, const void*, const void*, const float*, void*, SeqLayout, int, int, float,
+                              hipStream_t);
+template <int D>
+hipError_t launch_sm_bwd_fp32(const void*, const void*, const void*, const void*, const void*, void*, void*, void*,
+                              SeqLayout, int, int, float, float, hipStream_t);
 }  // namespace sigattn
 
 namespace {
@@ -68,10 +80,11 @@ int check_common(int Z, int L, int H, int D, float alpha, float bias, int dtype,
   if (!std::isfinite(alpha) || !std::isfinite(bias)) return fail(SIGATTN_EINVAL, "alpha and bias must be finite%s");
   if (Z == 0 || L == 0 || H == 0) return 1;
   if (nq == nullptr || nk == nullptr) return fail(SIGATTN_EINVAL, "seqlens_q and seqlens_k must not be NULL%s");
-  // Every kernel's grid is Z * H * ceil(L / 32) or fewer blocks, and element
-  // offsets are 64-bit. The grid must fit in 2^31 - 1 blocks.
-  const long long blocks = (long long)Z * H * ((L + 31) / 32);
-  if (blocks > 0x7fffffffLL) return fail(SIGATTN_EINVAL, "problem too large for one grid%s");
+  // The largest grid is Z * H * ceil(L / 256) blocks of 256 work-items (the
+  // fp32 kernels' 64-row tiles of 64 work-items need no more), and a dispatch
+  // holds at most 2^32 - 1 work-items. Element offsets are 64-bit.
+  const long long items = (long long)Z * H * ((L + 255) / 256) * 256;
+  if (items > 0xffffffffLL) return fail(SIGATTN_EINVAL, "problem too large for one grid%s");
   // Tiles reach LDS through buffer loads with 32-bit offsets below 256 rows.
   if ((long long)H * D * 2 * 256 >= 0x80000000LL) return fail(SIGATTN_EINVAL, "H * D too large%s");
   return 0;
@@ -104,8 +117,10 @@ int launch_dkdv(int mode, const void* q, const void* k, const void* v, const voi
   const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipError_t e;
   if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dkdv_bf16<128>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(0, mode, q, k, v, dout, dk, dv, nullptr, sl, Z, H, alpha, c1, c0,
+                                                  tc, st)
+                  : sigattn::launch_dkdv_bf16<128>(0, mode, q, k, v, dout, dk, dv, nullptr, sl, Z, H, alpha, c1, c0,
+                                                   tc, st);
   else
     e = (D == 64) ? sigattn::launch_dkdv_fp32<64>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st)
                   : sigattn::launch_dkdv_fp32<128>(mode, q, k, v, dout, dk, dv, sl, Z, H, alpha, c1, c0, tc, st);
@@ -117,8 +132,8 @@ int launch_dq(const void* q, const void* k, const void* v, const void* dout, voi
   const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
   hipError_t e;
   if (dtype == SIGATTN_BF16)
-    e = (D == 64) ? sigattn::launch_dq_bf16<64>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st)
-                  : sigattn::launch_dq_bf16<128>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st);
+    e = (D == 64) ? sigattn::launch_dq_bf16<64>(0, q, k, v, dout, dq, nullptr, sl, Z, H, alpha, c1, c0, tc, st)
+                  : sigattn::launch_dq_bf16<128>(0, q, k, v, dout, dq, nullptr, sl, Z, H, alpha, c1, c0, tc, st);
   else
     e = (D == 64) ? sigattn::launch_dq_fp32<64>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st)
                   : sigattn::launch_dq_fp32<128>(q, k, v, dout, dq, sl, Z, H, alpha, c1, c0, tc, st);
@@ -258,6 +273,79 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
     return rc;
   return launch_dq(q, k, v, dout, dq, padded(seqlens_q, seqlens_k, L), Z, H, D, alpha, bias, dtype, tile_counts_dq,
                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int sigattn_softmax_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* seq_q,
+                        const int32_t* seq_k, int layout, int Z, int L, int H, int D, float alpha, int dtype,
+                        void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
+  if (rc != 0) return rc;
+  if (!(alpha > 0.0f)) return fail(SIGATTN_EINVAL, "softmax needs alpha > 0%s");
+  rc = check_common(Z, L, H, D, alpha, 0.0f, dtype, seq_q, seq_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(o, "o")) || (rc = check_tensor(lse, "lse")))
+    return rc;
+  const sigattn::SeqLayout sl{seq_q, seq_k, L, layout, 0};
+  const float c1 = alpha * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == SIGATTN_BF16)
+    e = (D == 64) ? sigattn::launch_sm_fwd_bf16<64>(q, k, v, o, lse, sl, Z, H, c1, st)
+                  : sigattn::launch_sm_fwd_bf16<128>(q, k, v, o, lse, sl, Z, H, c1, st);
+  else
+    e = (D == 64) ? sigattn::launch_sm_fwd_fp32<64>(q, k, v, o, lse, sl, Z, H, c1, st)
+                  : sigattn::launch_sm_fwd_fp32<128>(q, k, v, o, lse, sl, Z, H, c1, st);
+  return hip_status(e);
+}
+
+size_t sigattn_softmax_bwd_workspace_size(long long rows_q, int H) {
+  return rows_q > 0 && H > 0 ? (size_t)rows_q * (size_t)H * 8 : 0;
+}
+
+int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, const int32_t* seq_q, const int32_t* seq_k,
+                        int layout, int Z, int L, int H, int D, float alpha, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
+  if (rc != 0) return rc;
+  if (!(alpha > 0.0f)) return fail(SIGATTN_EINVAL, "softmax needs alpha > 0%s");
+  rc = check_common(Z, L, H, D, alpha, 0.0f, dtype, seq_q, seq_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(o, "o")) || (rc = check_tensor(dout, "dout")) || (rc = check_tensor(lse, "lse")) ||
+      (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")) ||
+      (rc = check_tensor(workspace, "workspace")))
+    return rc;
+  // The padded layout has Z * L query rows. The packed layout's row count sits
+  // in device memory (the last offset): there only the one-row-per-sample floor
+  // is checked here, and the caller sizes the buffer for all of its rows.
+  const size_t rows = layout == SIGATTN_LAYOUT_PADDED ? (size_t)Z * L : (size_t)Z;
+  if (workspace_bytes < rows * (size_t)H * 8)
+    return fail(SIGATTN_EWORKSPACE, "workspace smaller than query rows * H * 8 bytes%s");
+  const sigattn::SeqLayout sl{seq_q, seq_k, L, layout, 0};
+  const float c1 = alpha * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int bf = dtype == SIGATTN_BF16;
+  hipError_t e = (D == 64) ? sigattn::launch_sm_rowstats<64>(bf, o, dout, lse, workspace, sl, Z, H, alpha, st)
+                           : sigattn::launch_sm_rowstats<128>(bf, o, dout, lse, workspace, sl, Z, H, alpha, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (bf) {
+    e = (D == 64) ? sigattn::launch_dkdv_bf16<64>(1, kKvBoth, q, k, v, dout, dk, dv, workspace, sl, Z, H, alpha, c1,
+                                                  0.0f, nullptr, st)
+                  : sigattn::launch_dkdv_bf16<128>(1, kKvBoth, q, k, v, dout, dk, dv, workspace, sl, Z, H, alpha, c1,
+                                                   0.0f, nullptr, st);
+    if (e != hipSuccess) return hip_status(e);
+    e = (D == 64) ? sigattn::launch_dq_bf16<64>(1, q, k, v, dout, dq, workspace, sl, Z, H, alpha, c1, 0.0f, nullptr, st)
+                  : sigattn::launch_dq_bf16<128>(1, q, k, v, dout, dq, workspace, sl, Z, H, alpha, c1, 0.0f, nullptr,
+                                                 st);
+  } else {
+    e = (D == 64) ? sigattn::launch_sm_bwd_fp32<64>(q, k, v, dout, workspace, dq, dk, dv, sl, Z, H, alpha, c1, st)
+                  : sigattn::launch_sm_bwd_fp32<128>(q, k, v, dout, workspace, dq, dk, dv, sl, Z, H, alpha, c1, st);
+  }
+  return hip_status(e);
 }
 
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype) {

@@ -1,457 +1,8 @@
-// Backward kernels of padding-aware sigmoid attention.
-//
-// Method (rainbus.top summary of arXiv:2604.27124, section "方法步骤详情", steps 4-5):
-//  - P = sigma(S) is recomputed from Q and K.
-//  - dS = P (1 - P) (dO V^T).
-//  - The backward is split into a dQ kernel and a dK/dV kernel. The dK/dV
-//    kernel takes the same product in the transposed view.
-//  - Neither kernel needs atomics.
-// The chain rule gives:
-//    dQ = alpha dS K,   dK = alpha dS^T Q,   dV = P^T dO.
-//
-// Padding: padded rows of K, V (keys >= n_k) and of Q, dO (queries >= n_q) are
-// never read. Their LDS rows are zeros. A zero V row gives dP = 0, so dS = 0,
-// and a zero dO row gives dP = 0 and adds P * 0 to dV. Padding therefore adds
-// exactly nothing to any valid gradient row. Tiles wholly in padding are skipped
-// and their output rows written as zeros.
-#include "common.hpp"
+// Backward: the fp32 validation kernels and the launchers of every backward
+// kernel. The bf16 kernels are templates in bwd_kernels.hpp.
+#include "bwd_kernels.hpp"
 
 namespace sigattn {
-
-template <int D>
-struct BwdCfg {
-  static constexpr int W = 64;          // rows a wave owns: queries (dQ kernel) or keys (dK/dV kernel)
-  static constexpr int NWAVE = 4;       // one wave per SIMD
-  static constexpr int BQ_DQ = 256;     // dQ kernel: query rows per workgroup
-  static constexpr int BK_DQ = 64;      // dQ kernel: keys per LDS tile
-  static constexpr int BK_KV = 256;     // dK/dV kernel: key rows per workgroup
-  static constexpr int BQ_KV = 64;      // dK/dV kernel: queries per LDS tile
-  static constexpr int KS = D / 16;     // MFMA k-steps over the head dim
-  static constexpr int NB = D / 32;     // 32-wide column blocks of the gradients
-  static constexpr int TILE = 64 * D;   // elements of one 64-row LDS tile (swizzled, unpadded)
-};
-
-// ------------------------------------------------------------------------------------------ dQ
-// Wave w owns 64 query rows (two 32-row blocks). It holds Q and dO as B
-// operands, for:
-//   S^T  = K Q^T   (A = K from LDS)
-//   dP^T = V dO^T  (A = V from LDS)
-// dS^T = P (1 - P) dP^T is built in registers and fed as the A operand of
-// dQ += dS K. That product takes K from LDS through transposed reads.
-// Key tiles of 64 rows stream through a 3-slot LDS ring by DMA. Per 32-key
-// block, the previous block's dQ MFMAs run beside this block's sigma and dS.
-// Tile t-2 is last read in iteration t-1 (the dQ of its second block), so the
-// DMA of tile t+1 into its slot starts only after iteration t's barrier.
-// Each slot is its own LDS variable and the key loop is unrolled by three, so
-// every LDS access names its slot at compile time. The compiler can then tell
-// the in-flight DMA apart from the reads of the other two slots and does not
-// wait for it before them.
-template <int D>
-__global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                                                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                                                      __bf16* __restrict__ dQ, SeqLayout sl, int Z, int H,
-                                                      float alpha, float c1, float c0_base,
-                                                      int32_t* __restrict__ tile_counts) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sK2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
-  __shared__ int rank_lds[kMaxRankedSamples];
-  const int n_qt = (sl.L + C::BQ_DQ - 1) / C::BQ_DQ;
-  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
-  const int z = tcd.z, h = tcd.h, m = tcd.m;
-  const int nq = sl.nq(z);
-  const int nk = sl.nk(z);
-  const float c0 = sl.c0_for(c0_base, nk);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const size_t rs = (size_t)H * D;
-  const size_t base = (sl.row0_q(z) * H + h) * D;    // Q, dO and dQ
-  const size_t base_k = (sl.row0_k(z) * H + h) * D;  // K and V
-  const int rows = sl.rows(nq);                       // rows of this sample in dQ
-  const int q0 = m * C::BQ_DQ;
-  __bf16* dQb = dQ + base;
-
-  if (q0 >= nq) {
-    const int rows_here = min(C::BQ_DQ, rows - q0);
-    const bf16x8 zz = zero_bf16x8();
-    for (int c = tid; c < rows_here * (D / 8); c += 256)
-      *(bf16x8*)(dQb + (size_t)(q0 + c / (D / 8)) * rs + (c % (D / 8)) * 8) = zz;
-    if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = 0;
-    return;
-  }
-
-  bf16x8 qf[2][C::KS], dof[2][C::KS];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qr = q0 + 64 * w + 32 * qb + l32;
-    const bool ok = qr < nq;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      qf[qb][s] = ok ? *(const bf16x8*)(Q + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
-      dof[qb][s] = ok ? *(const bf16x8*)(dO + base + (size_t)qr * rs + 16 * s + 8 * half) : zero_bf16x8();
-    }
-  }
-  f32x16 acc[2][C::NB];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.0f;
-
-  const int nkt = (nk + C::BK_DQ - 1) / C::BK_DQ;
-  const int nkt3 = (nkt + 2) / 3 * 3;
-  if (nkt > 0) {
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Kb = K + base_k;
-    const __bf16* Vb = V + base_k;
-    auto fetch = [&](__bf16* sk, __bf16* sv, int tile) {
-      const int k0 = tile * C::BK_DQ;
-      const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
-      dma_tile<D, 64, 256>(sk, Kb + off, row_bytes, nk - k0, tid);
-      dma_tile<D, 64, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
-    };
-    // The dQ of the previous 32-key block, beside this block's sigma and dS.
-    auto dq_mfmas = [&](const __bf16* kt, int kbp, const bf16x8 (&dsp)[2][2]) {
-#pragma unroll
-      for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 b = lds_tr<D>(kt, kbp * 32 + ks * 16, db * 32, lane);
-          acc[0][db] = mfma32(dsp[0][ks], b, acc[0][db]);
-          acc[1][db] = mfma32(dsp[1][ks], b, acc[1][db]);
-        }
-    };
-    // dS of the previous 32-key block, waiting for its dQ MFMAs (zero before the first block).
-    bf16x8 ds_prev[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) ds_prev[qb][0] = ds_prev[qb][1] = zero_bf16x8();
-    // One key tile in slot S; slot P holds the tile before it, slot N receives the next.
-    auto iteration = [&](auto s_c, auto p_c, auto n_c, int t) {
-      constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      __bf16* const sk = ring<S>(sK0, sK1, sK2);
-      __bf16* const sv = ring<S>(sV0, sV1, sV2);
-      const __bf16* const skp = ring<P>(sK0, sK1, sK2);
-      dma_wait();
-      __syncthreads();  // tile t is in LDS, and every wave is done with iteration t-1
-      if (t + 1 < nkt3) fetch(ring<N>(sK0, sK1, sK2), ring<N>(sV0, sV1, sV2), t + 1);  // slot N held tile t-2
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T, dP^T for this block (32 MFMAs)
-        f32x16 sacc[2], pacc[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 ak = lds_nat<D>(sk, kb * 32 + l32, 2 * s + half);
-          const bf16x8 av = lds_nat<D>(sv, kb * 32 + l32, 2 * s + half);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            sacc[qb] = mfma32(ak, qf[qb][s], sacc[qb]);
-            pacc[qb] = mfma32(av, dof[qb][s], pacc[qb]);
-          }
-        }
-        if (kb == 0)
-          dq_mfmas(skp, 1, ds_prev);
-        else
-          dq_mfmas(sk, 0, ds_prev);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = sigmoid_dot(sacc[qb][r], c1, c0);
-            ds_prev[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
-          }
-        interleave_mfma_valu<4 * C::KS + 2 * C::NB * 2, 6>();
-      }
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // Slot 2 stands in for tile -1: its reads are multiplied by ds_prev = 0, so
-    // it must hold finite values. It starts as zeros.
-    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sK2 + c * 8) = zero_bf16x8();
-    // The loop runs a multiple of three tiles. Tiles past n_k arrive as zeros
-    // (every DMA lane is out of range); a zero V row gives dP = 0 and so dS = 0,
-    // so they add exactly nothing.
-    fetch(sK0, sV0, 0);
-    for (int t = 0; t < nkt3; t += 3) {
-      iteration(I0{}, I2{}, I1{}, t);
-      iteration(I1{}, I0{}, I2{}, t + 1);
-      iteration(I2{}, I1{}, I0{}, t + 2);
-    }
-    dq_mfmas(sK2, 1, ds_prev);  // the last block, of tile nkt3 - 1 (slot 2)
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
-        if (row < rows) dQb[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? alpha * acc[qb][db][r] : 0.0f);
-      }
-  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
-}
-
-// ---------------------------------------------------------------------------------------- dK/dV
-// Wave w owns 64 key rows (two 32-row blocks). It holds K and V as B operands, for:
-//   S  = Q K^T   (A = Q from LDS)
-//   dP = dO V^T  (A = dO from LDS)
-// P^T and dS^T come straight from those accumulators as A operands, for:
-//   dV += P^T dO   (B = dO through transposed LDS reads)
-//   dK += dS^T Q   (B = Q through transposed LDS reads)
-// The query axis runs in blocks of 32, pipelined three deep as in the dQ
-// kernel:
-//   A: S (and dP) of block i
-//   B: dV (and dK) += ... of block i-2
-//   V: P (and dS) of block i-1
-// Query tiles of 64 rows reach a 3-slot LDS ring by DMA.
-//
-// MODE selects what one launch computes:
-//   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
-//   KV_DK (S, dP, dK: 6*D) and KV_DV (S, dV: 4*D) split the work over two
-//   launches.
-// At D = 128 the K and V operands plus both accumulators do not fit one
-// wave's registers (the fused form spills), so D = 128 runs the split form.
-enum KvMode { KV_BOTH = 0, KV_DK = 1, KV_DV = 2 };
-
-template <int D, int MODE, bool DO_A, bool DO_B, bool DO_V>
-__device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, int qba, const __bf16* sQb,
-                                        const __bf16* sGb, int qbb, f32x16 (&sN)[2], f32x16 (&pN)[2],
-                                        f32x16 (&dkacc)[2][BwdCfg<D>::NB], f32x16 (&dvacc)[2][BwdCfg<D>::NB],
-                                        const bf16x8 (&ptB)[2][2], const bf16x8 (&dsB)[2][2], bf16x8 (&ptV)[2][2],
-                                        bf16x8 (&dsV)[2][2], const f32x16 (&sV)[2], const f32x16 (&pV)[2],
-                                        const bf16x8 (&kf)[2][BwdCfg<D>::KS], const bf16x8 (&vf)[2][BwdCfg<D>::KS],
-                                        float c1, float c0, int l32, int half, int lane) {
-  using C = BwdCfg<D>;
-  constexpr bool DK = MODE != KV_DV, DV = MODE != KV_DK;
-  constexpr int PA = DK ? 2 : 1;                // A operands per k-step: Q (and dO)
-  constexpr int PB = (DK ? 1 : 0) + (DV ? 1 : 0);  // B operands per (db, ks): dO tr (dV), Q tr (dK)
-  constexpr int NA = DO_A ? PA * C::KS : 0;
-  constexpr int NSTEP = NA + (DO_B ? PB * 2 * C::NB : 0);
-  constexpr int NV = DO_V ? 32 : 0;
-  // which job operand j belongs to: 0 = Q nat, 1 = dO nat, 2 = dO tr, 3 = Q tr
-  auto kind = [](int j) constexpr -> int {
-    if (j < NA) return (PA == 2 && (j & 1)) ? 1 : 0;
-    const int i = j - NA;
-    if (PB == 2) return (i & 1) ? 3 : 2;
-    return DV ? 2 : 3;
-  };
-  auto read = [&](auto jc) -> bf16x8 {
-    constexpr int j = decltype(jc)::value;
-    constexpr int k = kind(j);
-    if constexpr (k <= 1) {
-      return lds_nat<D>(k == 1 ? sGa : sQa, qba * 32 + l32, 2 * (j / PA) + half);
-    } else {
-      constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
-      return lds_tr<D>(k == 2 ? sGb : sQb, qbb * 32 + ks * 16, db * 32, lane);
-    }
-  };
-  if constexpr (DO_A) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sN[0][r] = sN[1][r] = 0.0f;
-      if constexpr (DK) pN[0][r] = pN[1][r] = 0.0f;
-    }
-  }
-  bf16x8 ops[3];
-  ops[0] = read(std::integral_constant<int, 0>{});
-  ops[1] = read(std::integral_constant<int, 1>{});
-  static_for<0, NSTEP>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int k = kind(j);
-    if constexpr (j + 2 < NSTEP) ops[(j + 2) % 3] = read(std::integral_constant<int, j + 2>{});
-    const bf16x8 op = ops[j % 3];
-    if constexpr (k == 0) {
-      constexpr int s = j / PA;
-      sN[0] = mfma32(op, kf[0][s], sN[0]);
-      sN[1] = mfma32(op, kf[1][s], sN[1]);
-    } else if constexpr (k == 1) {
-      constexpr int s = j / PA;
-      pN[0] = mfma32(op, vf[0][s], pN[0]);
-      pN[1] = mfma32(op, vf[1][s], pN[1]);
-    } else {
-      constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
-      if constexpr (k == 2) {
-        dvacc[0][db] = mfma32(ptB[0][ks], op, dvacc[0][db]);
-        dvacc[1][db] = mfma32(ptB[1][ks], op, dvacc[1][db]);
-      } else {
-        dkacc[0][db] = mfma32(dsB[0][ks], op, dkacc[0][db]);
-        dkacc[1][db] = mfma32(dsB[1][ks], op, dkacc[1][db]);
-      }
-    }
-    constexpr int e0 = j * NV / NSTEP, e1 = (j + 1) * NV / NSTEP;
-    static_for<e0, e1>([&](auto ec) {
-      constexpr int e = decltype(ec)::value, kb = e >> 4, r = e & 15;
-      const float p = sigmoid_dot(sV[kb][r], c1, c0);
-      if constexpr (DV) ptV[kb][r >> 3][r & 7] = (__bf16)p;
-      if constexpr (DK) dsV[kb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pV[kb][r]);
-    });
-    constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
-    sched_step<j, nds, 2, (e1 - e0) * (DK ? 7 : 5), kNoFence>();  // a hard fence makes the dK kernel spill
-  });
-}
-
-// Whether the dK/dV query loop is unrolled over the three ring slots. Unrolled,
-// every LDS access names its slot at compile time, and the compiler does not
-// wait for the DMA into one slot before reading the others. That costs a few
-// registers (slot addresses past the 64 KB read offset range need their own),
-// which the two kernels already at the register limit (fused dK+dV at D = 64,
-// dK at D = 128) cannot spare: they keep a runtime slot index, and the compiler
-// waits for each DMA before their next LDS read.
-template <int D, int MODE>
-constexpr bool kUnrolledRing = !(MODE == KV_BOTH || (MODE == KV_DK && D == 128));
-
-// One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV).
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                                                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                                                        __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                                                        SeqLayout sl, int Z, int H, float alpha, float c1,
-                                                        float c0_base, int32_t* __restrict__ tile_counts) {
-  using C = BwdCfg<D>;
-  constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG2[C::TILE];
-  __shared__ int rank_lds[kMaxRankedSamples];
-  const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;
-  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, sl, rank_lds);
-  const int z = tcd.z, h = tcd.h, t = tcd.m;
-  const int nq = sl.nq(z);
-  const int nk = sl.nk(z);
-  const float c0 = sl.c0_for(c0_base, nk);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const size_t rs = (size_t)H * D;
-  const size_t base = (sl.row0_k(z) * H + h) * D;    // K, V, dK and dV
-  const size_t base_q = (sl.row0_q(z) * H + h) * D;  // Q and dO
-  const int rows = sl.rows(nk);                       // rows of this sample in dK, dV
-  const int k0 = t * C::BK_KV;
-  __bf16* dKb = dK + base;
-  __bf16* dVb = dV + base;
-
-  if (k0 >= nk) {
-    const int rows_here = min(C::BK_KV, rows - k0);
-    const bf16x8 zz = zero_bf16x8();
-    for (int c = tid; c < rows_here * (D / 8); c += 256) {
-      const size_t off = (size_t)(k0 + c / (D / 8)) * rs + (c % (D / 8)) * 8;
-      if (DO_DK) *(bf16x8*)(dKb + off) = zz;
-      if (DO_DV) *(bf16x8*)(dVb + off) = zz;
-    }
-    if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = 0;
-    return;
-  }
-
-  bf16x8 kf[2][C::KS], vf[2][C::KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int kr = k0 + 64 * w + 32 * kb + l32;
-    const bool ok = kr < nk;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      kf[kb][s] = ok ? *(const bf16x8*)(K + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
-      if (DO_DK) vf[kb][s] = ok ? *(const bf16x8*)(V + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
-    }
-  }
-  f32x16 dkacc[2][C::NB], dvacc[2][C::NB];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dkacc[kb][db][r] = dvacc[kb][db][r] = 0.0f;
-
-  const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
-  if (nqt > 0) {
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Qb = Q + base_q;
-    const __bf16* dOb = dO + base_q;
-    auto fetch = [&](__bf16* sq, __bf16* sg, int tile) {
-      const int r0 = tile * C::BQ_KV;
-      const size_t off = (size_t)(r0 < nq ? r0 : 0) * rs;  // no row is read past n_q
-      dma_tile<D, 64, 256>(sq, Qb + off, row_bytes, nq - r0, tid);
-      dma_tile<D, 64, 256>(sg, dOb + off, row_bytes, nq - r0, tid);
-    };
-    f32x16 sX[2], pX[2], sY[2], pY[2];
-    bf16x8 ptX[2][2], ptY[2][2], dsX[2][2], dsY[2][2];
-    // Query tile u: its slot (q_cur, g_cur), tile u-1's slot (q_prev, g_prev)
-    // and the slot that receives tile u+1 (it held tile u-2).
-    auto iteration = [&](__bf16* q_cur, __bf16* g_cur, __bf16* q_prev, __bf16* g_prev, __bf16* q_next,
-                         __bf16* g_next, int u, int n_tiles) {
-      dma_wait();
-      __syncthreads();
-      if (u + 1 < n_tiles) fetch(q_next, g_next, u + 1);
-      kv_step<D, MODE, true, true, true>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
-                                         dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
-      kv_step<D, MODE, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY, ptX,
-                                         dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
-    };
-    auto prologue = [&](int n_tiles) {
-      fetch(sQ0, sG0, 0);
-      dma_wait();
-      __syncthreads();
-      if (n_tiles > 1) fetch(sQ1, sG1, 1);  // no DMA may be left in flight when the kernel ends
-      kv_step<D, MODE, true, false, false>(sQ0, sG0, 0, sQ0, sG0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
-                                           pY, kf, vf, c1, c0, l32, half, lane);
-      kv_step<D, MODE, true, false, true>(sQ0, sG0, 1, sQ0, sG0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
-                                          pX, kf, vf, c1, c0, l32, half, lane);
-    };
-    auto epilogue = [&](__bf16* q_last, __bf16* g_last) {
-      kv_step<D, MODE, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY,
-                                          dsY, sY, pY, kf, vf, c1, c0, l32, half, lane);
-      kv_step<D, MODE, false, true, false>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY, dsY,
-                                           ptX, dsX, sX, pX, kf, vf, c1, c0, l32, half, lane);
-    };
-    if constexpr (kUnrolledRing<D, MODE>) {
-      // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
-      // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
-      // exactly nothing to dV or dK.
-      const int nqt3 = 1 + (nqt + 1) / 3 * 3;
-      prologue(nqt3);
-      for (int u = 1; u < nqt3; u += 3) {
-        iteration(sQ1, sG1, sQ0, sG0, sQ2, sG2, u, nqt3);
-        iteration(sQ2, sG2, sQ1, sG1, sQ0, sG0, u + 1, nqt3);
-        iteration(sQ0, sG0, sQ2, sG2, sQ1, sG1, u + 2, nqt3);
-      }
-      epilogue(sQ0, sG0);  // tile nqt3 - 1 sits in slot 0
-    } else {
-      auto q_at = [&](int i) { return i == 0 ? sQ0 : (i == 1 ? sQ1 : sQ2); };
-      auto g_at = [&](int i) { return i == 0 ? sG0 : (i == 1 ? sG1 : sG2); };
-      prologue(nqt);
-      int cur = 0;
-      for (int u = 1; u < nqt; ++u) {
-        const int prev = cur;
-        cur = (cur == 2) ? 0 : cur + 1;
-        const int next = (cur == 2) ? 0 : cur + 1;
-        iteration(q_at(cur), g_at(cur), q_at(prev), g_at(prev), q_at(next), g_at(next), u, nqt);
-      }
-      epilogue(q_at(cur), g_at(cur));
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = k0 + 64 * w + 32 * kb + acc_row(r, half);
-        if (row < rows) {
-          const bool ok = row < nk;
-          if (DO_DK) dKb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? alpha * dkacc[kb][db][r] : 0.0f);
-          if (DO_DV) dVb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? dvacc[kb][db][r] : 0.0f);
-        }
-      }
-  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = nqt;
-}
 
 // ------------------------------------------------------------------------------ fp32 validation
 // Scalar fp32. The dQ kernel has one thread per query row (BQ = 64, BK = 32).
@@ -588,34 +139,54 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(const float* __restrict__
 
 // --------------------------------------------------------------------------------- launchers
 // MODE: KV_BOTH (dk and dv), KV_DK (dk only) or KV_DV (dv only; v is not read).
+// act: ACT_SIGMOID (stats unused) or ACT_SOFTMAX (stats: {LSE / alpha, D} per query row and head).
 template <int D>
-hipError_t launch_dkdv_bf16(int mode, const void* q, const void* k, const void* v, const void* dout, void* dk,
-                            void* dv, SeqLayout sl, int Z, int H, float alpha, float c1, float c0, int32_t* tc,
-                            hipStream_t st) {
+hipError_t launch_dkdv_bf16(int act, int mode, const void* q, const void* k, const void* v, const void* dout,
+                            void* dk, void* dv, const void* stats, SeqLayout sl, int Z, int H, float alpha, float c1,
+                            float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
   const long long blocks = (long long)Z * H * ((sl.L + C::BK_KV - 1) / C::BK_KV);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, sl, Z, H, alpha, c1, c0, tc);
+                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, (const float2*)stats, sl, Z,
+                       H, alpha, c1, c0, tc);
     return hipGetLastError();
   };
-  if (mode == KV_DK) return go(dkdv_bf16_kernel<D, KV_DK>);
-  if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV>);
-  if constexpr (D == 64) return go(dkdv_bf16_kernel<D, KV_BOTH>);
-  // D = 128: the fused form does not fit a wave's registers. Both launches see
-  // the same lengths, so both write the same counters.
-  hipError_t e = go(dkdv_bf16_kernel<D, KV_DK>);
-  return e != hipSuccess ? e : go(dkdv_bf16_kernel<D, KV_DV>);
+  auto only_dk = [&](auto act_c) -> hipError_t {
+    constexpr int A = decltype(act_c)::value;
+    if constexpr (D == 128 && A == ACT_SOFTMAX)
+      return launch_dk_bf16_softmax_d128(q, k, v, dout, dk, stats, sl, Z, H, alpha, c1, tc, st);
+    else
+      return go(dkdv_bf16_kernel<D, KV_DK, A>);
+  };
+  auto run = [&](auto act_c) -> hipError_t {
+    constexpr int A = decltype(act_c)::value;
+    if (mode == KV_DK) return only_dk(act_c);
+    if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV, A>);
+    if constexpr (D == 64 && A == ACT_SIGMOID) return go(dkdv_bf16_kernel<D, KV_BOTH, A>);
+    // D = 128, and softmax at D = 64 (its row statistics add registers): the
+    // fused form does not fit a wave's registers. Both launches see the same
+    // lengths, so both write the same counters.
+    hipError_t e = only_dk(act_c);
+    return e != hipSuccess ? e : go(dkdv_bf16_kernel<D, KV_DV, A>);
+  };
+  return act == ACT_SOFTMAX ? run(std::integral_constant<int, ACT_SOFTMAX>{})
+                            : run(std::integral_constant<int, ACT_SIGMOID>{});
 }
 
 template <int D>
-hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dout, void* dq, SeqLayout sl,
-                          int Z, int H, float alpha, float c1, float c0, int32_t* tc, hipStream_t st) {
+hipError_t launch_dq_bf16(int act, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                          const void* stats, SeqLayout sl, int Z, int H, float alpha, float c1, float c0,
+                          int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
   const long long blocks = (long long)Z * H * ((sl.L + C::BQ_DQ - 1) / C::BQ_DQ);
-  hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, sl, Z, H, alpha, c1, c0, tc);
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dq, (const float2*)stats, sl, Z, H, alpha, c1,
+                       c0, tc);
+    return hipGetLastError();
+  };
+  return act == ACT_SOFTMAX ? go(dq_bf16_kernel<D, ACT_SOFTMAX>) : go(dq_bf16_kernel<D, ACT_SIGMOID>);
 }
 
 template <int D>
@@ -640,12 +211,14 @@ hipError_t launch_dq_fp32(const void* q, const void* k, const void* v, const voi
 }
 
 #define SIGATTN_INST_BWD(D)                                                                                        \
-  template hipError_t launch_dkdv_bf16<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
-                                          SeqLayout, int, int, float, float, float, int32_t*, hipStream_t);     \
+  template hipError_t launch_dkdv_bf16<D>(int, int, const void*, const void*, const void*, const void*, void*,   \
+                                          void*, const void*, SeqLayout, int, int, float, float, float, int32_t*, \
+                                          hipStream_t);                                                         \
   template hipError_t launch_dkdv_fp32<D>(int, const void*, const void*, const void*, const void*, void*, void*, \
                                           SeqLayout, int, int, float, float, float, int32_t*, hipStream_t);     \
-  template hipError_t launch_dq_bf16<D>(const void*, const void*, const void*, const void*, void*, SeqLayout,    \
-                                        int, int, float, float, float, int32_t*, hipStream_t);                  \
+  template hipError_t launch_dq_bf16<D>(int, const void*, const void*, const void*, const void*, void*,          \
+                                        const void*, SeqLayout, int, int, float, float, float, int32_t*,        \
+                                        hipStream_t);                                                           \
   template hipError_t launch_dq_fp32<D>(const void*, const void*, const void*, const void*, void*, SeqLayout,    \
                                         int, int, float, float, float, int32_t*, hipStream_t);
 SIGATTN_INST_BWD(64)

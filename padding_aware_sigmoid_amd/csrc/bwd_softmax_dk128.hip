@@ -1,0 +1,20 @@
+// The softmax dK kernel at D = 128 (dK only; dV runs as its own launch).
+// It is the backward's one kernel that the compiler cannot build with MFMA
+// results in VGPRs at its register count, so this file is built without that
+// option (accumulators in AGPRs).
+#include "bwd_kernels.hpp"
+
+namespace sigattn {
+
+hipError_t launch_dk_bf16_softmax_d128(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                                       const void* stats, SeqLayout sl, int Z, int H, float alpha, float c1,
+                                       int32_t* tc, hipStream_t st) {
+  using C = BwdCfg<128>;
+  const long long blocks = (long long)Z * H * ((sl.L + C::BK_KV - 1) / C::BK_KV);
+  hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DK, ACT_SOFTMAX>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk,
+                     (__bf16*)nullptr, (const float2*)stats, sl, Z, H, alpha, c1, 0.0f, tc);
+  return hipGetLastError();
+}
+
+}  // namespace sigattn

@@ -9,6 +9,7 @@
 namespace sigattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -359,6 +360,22 @@ __device__ __forceinline__ void dma_tile_chunk(__bf16* tile, const __bf16* rows,
   const int c = cs ^ Tile<D>::swz(r);
   const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
   llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16), 16,
+                                  (int)voff, 0, 0, 0);
+}
+
+// DMA 64 rows of a float2 row statistic into LDS as float2[64] (512 B). Row r
+// of the source sits at byte r * stride_bytes; rows at or past n_valid arrive
+// as zeros. Waves 0 and 1 each issue one 4-byte-per-lane instruction (floats
+// 0..63, then 64..127); other waves issue nothing.
+__device__ __forceinline__ void dma_stats64(float2* dst, const float2* src, uint32_t stride_bytes, int n_valid,
+                                            int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  if (w >= 2) return;
+  const int nv = n_valid < 0 ? 0 : (n_valid > 64 ? 64 : n_valid);
+  const i32x4 rsrc = make_rsrc(src, nv > 0 ? (uint32_t)(nv - 1) * stride_bytes + 8 : 0u);
+  const int f = w * 64 + lane, row = f >> 1;
+  const uint32_t voff = row < nv ? (uint32_t)row * stride_bytes + (uint32_t)(f & 1) * 4 : kOutOfRange;
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)dst + w * 256), 4,
                                   (int)voff, 0, 0, 0);
 }
 

@@ -346,3 +346,109 @@ def sigmoid_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha
                              bias_mode="constant"):
     """Differentiable sigmoid attention over packed [T, H, D] sequences."""
     return SigmoidAttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha, bias, bias_mode)
+
+
+# ------------------------------------------------------------------------------------- softmax attention
+
+
+def _softmax_layout(q, k, seq_q, seq_k, max_len, named_q: dict, named_k: dict):
+    """(layout, Z, L, seq_q, seq_k): padded [Z, L, H, D] tensors with lengths, or
+    packed [T, H, D] tensors with int32[Z + 1] offsets and max_len."""
+    if q.dim() == 4:
+        _check_tensors(q, {"k": k, **named_q, **named_k})
+        Z, L = q.shape[0], q.shape[1]
+        return _lib.LAYOUT_PADDED, Z, L, _lengths(seq_q, Z, q.device), _lengths(seq_k, Z, q.device)
+    if max_len is None:
+        raise ValueError("packed [T, H, D] tensors need max_len")
+    _check_packed(q, k, named_q, named_k)
+    cq, ck = _offsets(seq_q, q.device), _offsets(seq_k, q.device)
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
+    return _lib.LAYOUT_PACKED, cq.numel() - 1, int(max_len), cq, ck
+
+
+def _check_lse(lse, q):
+    want = q.shape[:-1]
+    if lse.shape != want or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(want)} on q's device")
+
+
+def sigattn_softmax_fwd(q, k, v, seq_q, seq_k, alpha=None, out=None, lse=None, max_len=None):
+    """(O, LSE) of padding-aware softmax attention. Wraps sigattn_softmax_fwd.
+
+    Padded: q, k, v [Z, L, H, D], seq_* int32[Z] lengths. Packed: q [Tq, H, D],
+    k, v [Tk, H, D], seq_* int32[Z + 1] offsets, max_len bounding every length.
+    LSE (natural log, fp32) has q's shape without D. alpha defaults to 1/sqrt(D).
+    """
+    layout, Z, L, sq, sk = _softmax_layout(q, k, seq_q, seq_k, max_len, {}, {"v": v})
+    H, D = q.shape[-2], q.shape[-1]
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must match q in shape, dtype and device and be contiguous")
+    _check_lse(lse, q)
+    _lib.check(_lib.load().sigattn_softmax_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                               lse.data_ptr(), sq.data_ptr(), sk.data_ptr(), layout, Z, L, H, D,
+                                               alpha, _dtype_code(q), _stream(q.device)))
+    return o, lse
+
+
+def sigattn_softmax_bwd(q, k, v, o, dout, lse, seq_q, seq_k, alpha=None, dq=None, dk=None, dv=None, max_len=None,
+                        workspace=None):
+    """(dq, dk, dv) of padding-aware softmax attention from the forward's O and
+    LSE. Wraps sigattn_softmax_bwd; layouts as for sigattn_softmax_fwd. The
+    workspace (rows_q * H * 8 bytes) is allocated here unless given."""
+    layout, Z, L, sq, sk = _softmax_layout(q, k, seq_q, seq_k, max_len, {"o": o, "dout": dout}, {"v": v})
+    H, D = q.shape[-2], q.shape[-1]
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    _check_lse(lse, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+            raise ValueError(f"{name} must match {'q' if ref is q else 'k'} in shape, dtype and device")
+    lib = _lib.load()
+    rows = q.shape[0] * q.shape[1] if layout == _lib.LAYOUT_PADDED else q.shape[0]
+    nbytes = lib.sigattn_softmax_bwd_workspace_size(rows, H)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    _lib.check(lib.sigattn_softmax_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), sq.data_ptr(),
+                                       sk.data_ptr(), layout, Z, L, H, D, alpha, _dtype_code(q),
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(q.device)))
+    return dq, dk, dv
+
+
+class SoftmaxAttention(torch.autograd.Function):
+    """Autograd wrapper of the softmax path. The forward saves its inputs, O and
+    LSE; the backward recomputes P from them."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, seq_q, seq_k, alpha=None, max_len=None):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        layout, _, _, sq, sk = _softmax_layout(q, k, seq_q, seq_k, max_len, {}, {"v": v})
+        alpha = default_alpha(q.shape[-1]) if alpha is None else float(alpha)
+        o, lse = sigattn_softmax_fwd(q, k, v, sq, sk, alpha, max_len=max_len)
+        ctx.save_for_backward(q, k, v, o, lse, sq, sk)
+        ctx.scalars = (alpha, max_len)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, grad_out, grad_lse):
+        q, k, v, o, lse, sq, sk = ctx.saved_tensors
+        alpha, max_len = ctx.scalars
+        dq, dk, dv = sigattn_softmax_bwd(q, k, v, o, grad_out.contiguous(), lse, sq, sk, alpha, max_len=max_len)
+        return dq, dk, dv, None, None, None, None
+
+
+def softmax_attention(q, k, v, seq_q, seq_k, alpha=None, max_len=None):
+    """Differentiable padding-aware softmax attention: returns O (LSE is not
+    differentiated). Padded [Z, L, H, D] with lengths, or packed [T, H, D] with
+    offsets and max_len."""
+    return SoftmaxAttention.apply(q, k, v, seq_q, seq_k, alpha, max_len)[0]

@@ -100,3 +100,36 @@ def test_strings_and_configs(lib):
     with pytest.raises(_lib.SigattnError):
         _lib.tile_config(5, 64, 0)
     assert _lib.workspace_size(0, 1, 16384, 16, 128, 0) == 0
+
+
+def test_softmax_argument_errors_need_no_gpu(lib):
+    null, f = None, ctypes.c_void_p(16)
+    fwd = lib.sigattn_softmax_fwd
+    bwd = lib.sigattn_softmax_bwd
+    # alpha must be > 0 (the running row maximum assumes it)
+    for a in (0.0, -1.0, float("nan")):
+        assert fwd(f, f, f, f, f, f, f, 0, 1, 8, 1, 64, a, 0, null) == -1
+        assert b"alpha > 0" in lib.sigattn_last_error()
+    assert fwd(f, f, f, f, f, f, f, 2, 1, 8, 1, 64, 1.0, 0, null) == -1
+    assert b"layout" in lib.sigattn_last_error()
+    assert fwd(f, f, f, f, f, f, f, 0, 1, 8, 1, 96, 1.0, 0, null) == -1
+    assert fwd(f, f, f, f, f, f, f, 0, 1, 8, 1, 64, 1.0, 7, null) == -2
+    # NULL lse
+    assert fwd(f, f, f, f, null, f, f, 0, 1, 8, 1, 64, 1.0, 0, null) == -1
+    assert b"lse" in lib.sigattn_last_error()
+    # empty batch: nothing to do
+    assert fwd(null, null, null, null, null, null, null, 0, 0, 8, 1, 64, 1.0, 0, null) == 0
+    # backward: NULL workspace, then one too small for Z * L * H rows (padded)
+    assert bwd(f, f, f, f, f, f, f, f, f, f, f, 0, 2, 8, 3, 64, 1.0, 0, null, 0, null) == -1
+    assert b"workspace" in lib.sigattn_last_error()
+    assert bwd(f, f, f, f, f, f, f, f, f, f, f, 0, 2, 8, 3, 64, 1.0, 0, f, 2 * 8 * 3 * 8 - 1, null) == -4
+    assert bwd(f, f, f, f, f, f, f, f, f, f, f, 0, 2, 8, 3, 64, 0.0, 0, f, 1 << 20, null) == -1
+    assert lib.sigattn_softmax_bwd_workspace_size(2 * 8, 3) == 2 * 8 * 3 * 8
+    assert lib.sigattn_softmax_bwd_workspace_size(0, 3) == 0
+
+
+def test_grid_limit(lib):
+    # 2^20 samples of 2^16 rows: more work-items than one dispatch holds
+    null, f = None, ctypes.c_void_p(16)
+    assert lib.sigattn_fwd(f, f, f, f, f, f, 1 << 20, 1 << 16, 1, 64, 1.0, 0.0, 0, null, 0, null, null) == -1
+    assert b"too large" in lib.sigattn_last_error()
