@@ -18,6 +18,9 @@ Definitions:
   sample. The pages report both no padding and 25% padding.
 * `varlen`: the cell-batch workload (71% padded tokens) timed fwd+bwd in the
   padded layout and in the packed layout on the same valid rows.
+* `softmax`: padding-aware softmax attention fwd+bwd on the main workload,
+  with the same FLOP count, timed per call (forward: one kernel; backward:
+  row statistics, dK, dV, dQ) with HIP events on the launch stream.
 
 One GPU only. --gpus above 1 exits with a message.
 """
@@ -47,6 +50,8 @@ def parse():
     ap.add_argument("--pad-workload", default="pad25_16k", help="secondary workload reported in the same line ('' to skip)")
     ap.add_argument("--varlen-workload", default="cellbatch8k",
                     help="workload timed in the padded and the packed layout ('none' skips)")
+    ap.add_argument("--softmax-workload", default="nopad16k",
+                    help="workload of the softmax fwd+bwd sub-object ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many bytes twice (a plain device copy of "
@@ -189,6 +194,52 @@ def run_layouts(name, steps, warmup, seed=0):
     return out
 
 
+def run_softmax(name, steps, warmup, seed=0):
+    """Softmax attention fwd + bwd (padded layout) on one workload: ms per
+    forward call and per backward call, from HIP events on the launch stream,
+    and TFLOP/s counted as for sigmoid attention (valid tokens, bwd = 2.5x fwd)."""
+    import torch
+
+    import padding_aware_sigmoid_amd as sa
+    import workloads
+    from padding_aware_sigmoid_amd import accounting
+
+    inp = workloads.make_inputs(name, seed=seed)
+    w = inp["workload"]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    nq = torch.as_tensor(inp["seqlens_q"]).to(dev)
+    nk = torch.as_tensor(inp["seqlens_k"]).to(dev)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    ws = torch.empty(w.Z * w.L * w.H * 8, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = [lambda: sa.sigattn_softmax_fwd(q, k, v, nq, nk, w.alpha, out=o, lse=lse),
+             lambda: sa.sigattn_softmax_bwd(q, k, v, o, do, lse, nq, nk, w.alpha, dq=dq, dk=dk, dv=dv, workspace=ws)]
+    for _ in range(warmup):
+        for fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        for i, fn in enumerate(calls):
+            e[i].record(stream)
+            fn()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fl = accounting.attention_flops(w.Z, w.L, w.H, w.D, inp["seqlens_q"], inp["seqlens_k"])
+    out = {"workload": w.name, "Z": w.Z, "H": w.H, "L": w.L, "D": w.D, "alpha": w.alpha,
+           "ms_per_step": round(t_fwd + t_bwd, 4), "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+           "tflops_valid": round(fl["total_valid"] / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
+           "fwd_tflops_valid": round(fl["fwd_valid"] / (t_fwd * 1e-3) / 1e12, 2),
+           "bwd_tflops_valid": round(fl["bwd_valid"] / (t_bwd * 1e-3) / 1e12, 2)}
+    del q, k, v, do, o, dq, dk, dv, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name, heads=2):
     """The oracle, as it stands, on `heads` (z, h) heads of the workload at full length: fwd + bwd."""
     import numpy as np
@@ -292,6 +343,11 @@ def main():
         }
     if args.varlen_workload not in ("", "none"):
         line["varlen"] = run_layouts(args.varlen_workload, args.steps, args.warmup)
+    if args.softmax_workload not in ("", "none"):
+        sm = run_softmax(args.softmax_workload, args.steps, args.warmup)
+        if args.softmax_workload == args.workload:
+            sm["sigmoid_speedup"] = round(sm["ms_per_step"] / main_res["ms_per_step"], 3)
+        line["softmax"] = sm
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)

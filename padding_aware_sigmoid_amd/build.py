@@ -20,6 +20,10 @@ LIB = PKG / "libsigattn.so"
 SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "bwd_softmax_dk128.hip", "softmax.hip"]
 # Sources built without the VGPR form of MFMA results (see the file's header).
 AGPR_FORM_SOURCES = {"bwd_softmax_dk128.hip"}
+# Per-source extra flags. The softmax dK kernel at D = 128 sits at the register
+# limit: the max-ILP scheduler leaves it with no spill (the default scheduler
+# spills 5 VGPRs) and measured 0.66 ms faster per call at L = 16K, H = 16.
+EXTRA_FLAGS = {"bwd_softmax_dk128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -59,7 +63,7 @@ def build(verbose: bool = False) -> pathlib.Path:
     jobs = []
     for src in SOURCES:
         obj = objdir / (pathlib.Path(src).stem + ".o")
-        flags = COMMON_FLAGS + ([] if src in AGPR_FORM_SOURCES else VGPR_FORM)
+        flags = COMMON_FLAGS + ([] if src in AGPR_FORM_SOURCES else VGPR_FORM) + EXTRA_FLAGS.get(src, [])
         jobs.append((obj, [cc, *flags, "-c", str(CSRC / src), "-o", str(obj)]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):

@@ -1,7 +1,9 @@
 // The softmax dK kernel at D = 128 (dK only; dV runs as its own launch).
-// It is the backward's one kernel that the compiler cannot build with MFMA
-// results in VGPRs at its register count, so this file is built without that
-// option (accumulators in AGPRs).
+// It holds K and V for 64 keys, the dK accumulators and two blocks of S and
+// dP, at the 512-register limit. With MFMA results in VGPRs the compiler
+// fails on it among the other backward kernels and spills 350 registers on
+// its own, so this file is built with accumulators in AGPRs and the max-ILP
+// scheduler, which leaves no spill.
 #include "bwd_kernels.hpp"
 
 namespace sigattn {

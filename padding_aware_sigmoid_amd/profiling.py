@@ -26,7 +26,8 @@ import sys
 
 ROOT = pathlib.Path(__file__).resolve().parent.parent
 KERNEL_SOURCES = ["padding_aware_sigmoid_amd/csrc/common.hpp", "padding_aware_sigmoid_amd/csrc/fwd.hip",
-                  "padding_aware_sigmoid_amd/csrc/bwd.hip"]
+                  "padding_aware_sigmoid_amd/csrc/bwd_kernels.hpp", "padding_aware_sigmoid_amd/csrc/bwd.hip",
+                  "padding_aware_sigmoid_amd/csrc/bwd_softmax_dk128.hip", "padding_aware_sigmoid_amd/csrc/softmax.hip"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -38,16 +39,35 @@ def kernel_source_hash() -> str:
 
 
 def short_name(kernel: str) -> str | None:
-    """The bench name of a sigattn kernel from its demangled name, else None."""
-    m = re.search(r"sigattn::(fwd|dq|dkdv)_(bf16|fp32)_kernel<(\d+)(?:,\s*(\d))?>", kernel)
-    if m is None:  # the mangled form, e.g. _ZN7sigattn16dkdv_bf16_kernelILi128ELi2EEEv...
-        m = re.search(r"_ZN7sigattn\d+(fwd|dq|dkdv)_(bf16|fp32)_kernelILi(\d+)E(?:Li(\d)E)?", kernel)
-    if m is None:
+    """The bench name of a sigattn kernel from its demangled or mangled name,
+    else None. Sigmoid bf16: fwd, dq, dk, dv, dkdv; softmax: the same with an
+    sm_ prefix, plus sm_rowstats; fp32 kernels carry a _fp32 suffix."""
+    m = re.search(r"sigattn::(\w+?)_kernel<([^>]*)>", kernel)
+    if m is not None:
+        base, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+        ints = [int(a) for a in args if a.isdigit()]
+        float_arg = "float" in args
+    else:  # e.g. _ZN7sigattn16dkdv_bf16_kernelILi128ELi1ELi0EEEv...
+        m = re.search(r"_ZN7sigattn\d+(\w+?)_kernelI(.*?)EEv", kernel)
+        if m is None:
+            return None
+        base = m.group(1)
+        ints = [int(x) for x in re.findall(r"Li(\d+)E", m.group(2))]
+        float_arg = m.group(2).startswith("f")
+    sm = base.startswith("sm_")
+    core = base[3:] if sm else base
+    if core == "rowstats":
+        return "sm_rowstats" + ("_fp32" if float_arg else "")
+    mk = re.fullmatch(r"(fwd|dq|dkdv)_(bf16|fp32)", core)
+    if mk is None:
         return None
-    kind, dtype, _, mode = m.groups()
-    if kind == "dkdv" and mode is not None:
-        kind = {"0": "dkdv", "1": "dk", "2": "dv"}[mode]
-    return kind if dtype == "bf16" else f"{kind}_fp32"
+    kind, dtype = mk.groups()
+    if dtype == "bf16" and kind == "dq" and len(ints) > 1:
+        sm = sm or ints[1] == 1
+    if dtype == "bf16" and kind == "dkdv" and len(ints) > 1:
+        kind = {0: "dkdv", 1: "dk", 2: "dv"}[ints[1]]
+        sm = sm or (len(ints) > 2 and ints[2] == 1)
+    return ("sm_" if sm else "") + kind + ("" if dtype == "bf16" else "_fp32")
 
 
 def _csv(path: pathlib.Path, suffix: str) -> list[dict]:

@@ -67,3 +67,29 @@ def test_flop_rule():
     n = workloads.lengths(w, 0)
     h = accounting.attention_flops(w.Z, w.L, w.H, w.D, n, n)
     assert math.isclose(h["fwd_valid"] / 1e12, 5.157, rel_tol=1e-3)
+
+
+def test_profile_kernel_names():
+    from padding_aware_sigmoid_amd.profiling import short_name
+
+    cases = {
+        "void sigattn::fwd_bf16_kernel<128>(...)": "fwd",
+        "void sigattn::dkdv_bf16_kernel<128, 1, 0>(...)": "dk",
+        "void sigattn::dkdv_bf16_kernel<128, 2, 1>(...)": "sm_dv",
+        "void sigattn::dkdv_bf16_kernel<64, 0, 0>(...)": "dkdv",
+        "void sigattn::dq_bf16_kernel<128, 1>(...)": "sm_dq",
+        "void sigattn::dq_bf16_kernel<64, 0>(...)": "dq",
+        "void sigattn::sm_fwd_bf16_kernel<128>(...)": "sm_fwd",
+        "void sigattn::sm_rowstats_kernel<__bf16, 128>(...)": "sm_rowstats",
+        "void sigattn::sm_rowstats_kernel<float, 64>(...)": "sm_rowstats_fp32",
+        "void sigattn::dq_fp32_kernel<64>(...)": "dq_fp32",
+        "void sigattn::sm_dkdv_fp32_kernel<128>(...)": "sm_dkdv_fp32",
+        "_ZN7sigattn16dkdv_bf16_kernelILi128ELi1ELi1EEEvPKDF16b": "sm_dk",
+        "_ZN7sigattn16dkdv_bf16_kernelILi128ELi2ELi0EEEvPKDF16b": "dv",
+        "_ZN7sigattn14dq_bf16_kernelILi128ELi0EEEvPKDF16b": "dq",
+        "_ZN7sigattn18sm_rowstats_kernelIDF16bLi128EEEvPKT_": "sm_rowstats",
+        "_ZN7sigattn18sm_fwd_bf16_kernelILi64EEEvPKDF16b": "sm_fwd",
+        "__amd_rocclr_copyBuffer": None,
+    }
+    for name, want in cases.items():
+        assert short_name(name) == want, name
