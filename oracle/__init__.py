@@ -4,6 +4,7 @@ Only the tests, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this package. The library never does.
 """
 
+from . import fp8_attention  # noqa: F401  (fp8_attention.quantize, .forward, ...)
 from . import softmax_attention  # noqa: F401  (softmax_attention.forward, .backward, ...)
 from .sigmoid_attention import (  # noqa: F401
     backward,

@@ -20,6 +20,7 @@ import pathlib
 
 import numpy as np
 
+from oracle import fp8_attention as f8a
 from oracle import sigmoid_attention as osa
 from oracle import softmax_attention as sma
 
@@ -621,6 +622,166 @@ def pin_softmax_finite_differences():
             assert abs(fd - grad[idx]) < 1e-7, f"softmax {name}{idx}: fd {fd} vs {grad[idx]}"
 
 
+# ------------------------------------------------------------------------------ FP8 path
+# OCP 8-bit floating point, E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9,
+# largest finite 1.75 * 2^8 = 448, code 0x7f NaN (the OCP FP8 specification's
+# E4M3 table). Every expected value below is read off that definition.
+def pin_e4m3_format():
+    """Known codes of the E4M3 table, an exact round trip of every finite code,
+    a strictly increasing grid, and round-to-nearest-even at every midpoint."""
+    table = {0x00: 0.0, 0x01: 2.0**-9, 0x07: 7 * 2.0**-9, 0x08: 2.0**-6, 0x38: 1.0, 0x3A: 1.25, 0x40: 2.0,
+             0x70: 128.0, 0x77: 240.0, 0x7E: 448.0, 0xC2: -2.5, 0xB8: -1.0, 0xFE: -448.0}
+    for code, val in table.items():
+        assert f8a.e4m3_decode(np.uint8(code)) == val, f"decode 0x{code:02x}"
+        assert int(f8a.e4m3_encode(val)) == code, f"encode {val}"
+    assert np.isnan(f8a.e4m3_decode(np.uint8(0x7F))) and np.isnan(f8a.e4m3_decode(np.uint8(0xFF)))
+    assert int(f8a.e4m3_encode(-0.0)) == 0x80
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    assert np.array_equal(f8a.e4m3_encode(f8a.e4m3_decode(codes)), codes), "codes do not round-trip"
+    pos = f8a.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0), "grid not increasing"
+    lo, hi = pos[:-1], pos[1:]
+    mid = (lo + hi) / 2
+    even = np.where(np.arange(0x00, 0x7E) % 2 == 0, lo, hi)   # the neighbour with an even code
+    _close(f8a.e4m3_round(mid), even, rtol=0, atol=0, what="ties to even")
+    _close(f8a.e4m3_round(-mid), -even, rtol=0, atol=0, what="ties to even, negative")
+    _close(f8a.e4m3_round(mid - (hi - lo) / 8), lo, rtol=0, atol=0, what="below a midpoint")
+    _close(f8a.e4m3_round(mid + (hi - lo) / 8), hi, rtol=0, atol=0, what="above a midpoint")
+    _close(f8a.e4m3_round([1.0625, 1.1875, 1.5 * 2.0**-9, 2.0**-10]), [1.0, 1.25, 2.0**-8, 0.0], rtol=0, atol=0,
+           what="rounding examples")
+
+
+def pin_fp8_quantize():
+    """Per-tile power-of-two quantisation: a hand-worked tile, exact round trips
+    of representable values, the E4M3 error bound, per-tile independence, and
+    zero codes for padding."""
+    Z, L, H, D = 2, 150, 2, 8
+    n = [150, 70]
+    x = np.zeros((Z, L, H, D))
+    # tile 0 of (0, 0): amax 1 -> E = -7 (1 * 2^7 = 128 in [128, 256)), byte 120
+    x[0, 0:64, 0, 0] = 1.0
+    x[0, 0:64, 0, 1] = 0.5          # 64 -> code 0x68
+    x[0, 0:64, 0, 2] = -3 / 128     # -3 = -1.5 * 2^1 -> exponent field 8, mantissa 4: code 0xc4
+    codes, sb = f8a.quantize(x, n)
+    assert sb[0, 0, 0] == 120, f"scale byte {sb[0, 0, 0]}"
+    assert codes[0, 5, 0, 0] == 0x70 and codes[0, 5, 0, 1] == 0x68 and codes[0, 5, 0, 2] == 0xC4
+    # all-zero tiles: E = 0, byte 127, codes 0
+    assert sb[0, 1, 0] == 127 and not codes[0, :64, 1].any()
+    # representable values round-trip exactly; others stay within 2^-4 (normal) or 2^-10 2^E (subnormal)
+    rng = np.random.default_rng(80)
+    y = rng.standard_normal((Z, L, H, D)) * np.exp(rng.uniform(-6, 6, (Z, 1, H, 1)))
+    cy, sy = f8a.quantize(y, n)
+    dy = f8a.dequantize(cy, sy)
+    again, s_again = f8a.quantize(dy, n)
+    for z in range(Z):
+        for h in range(H):
+            for m in range(-(-n[z] // 64)):
+                r0, r1 = 64 * m, min(64 * m + 64, n[z])
+                e = int(sy[z, h, m]) - 127
+                blk, got = y[z, r0:r1, h], dy[z, r0:r1, h]
+                assert 128 <= np.max(np.abs(blk)) * 2.0**-e < 256, "amax not mapped into [128, 256)"
+                tol = np.where(np.abs(blk) * 2.0**-e >= 2.0**-6, 2.0**-4 * np.abs(blk), 2.0**(e - 10))
+                assert np.all(np.abs(got - blk) <= tol), "quantisation error beyond the E4M3 bound"
+                if s_again[z, h, m] == sy[z, h, m]:
+                    assert np.array_equal(again[z, r0:r1, h], cy[z, r0:r1, h]), "representable values moved"
+                else:  # the tile's amax rounded up to 256 * 2^E, one binade higher
+                    assert s_again[z, h, m] == sy[z, h, m] + 1 and np.max(np.abs(got)) * 2.0**-e == 256
+    assert not cy[1, 70:].any(), "padded rows have non-zero codes"
+    # scaling one tile by 2^5 moves only its byte
+    y2 = y.copy()
+    y2[1, 0:64, 1] *= 32.0
+    c2, s2 = f8a.quantize(y2, n)
+    assert np.array_equal(c2, cy) and s2[1, 1, 0] == sy[1, 1, 0] + 5
+    s2[1, 1, 0] -= 5
+    assert np.array_equal(s2, sy)
+
+
+def _fp8_inputs(V, nq, nk, Z, L, H, D, q=None, k=None):
+    q = np.zeros((Z, L, H, D)) if q is None else q
+    k = np.zeros((Z, L, H, D)) if k is None else k
+    q8, sq = f8a.quantize(q, nq)
+    k8, sk = f8a.quantize(k, nk)
+    v8, sv = f8a.quantize(V, nk)
+    return q8, k8, v8, sq, sk, sv
+
+
+def pin_fp8_forward_closed_forms():
+    """Q = 0 gives P = sigma(b) on every valid key. sigma(ln 3) = 3/4 = 192 * 2^-8
+    is on the E4M3 grid, so P is exact; sigma(ln 7/3) = 0.7: 0.7 * 2^8 = 179.2
+    lies between 176 and 192 (step 16 in [128, 256)), so P becomes 176/256 =
+    11/16. V holds values of at most two significant bits, exactly
+    representable at every power-of-two scale, so O is 11/16 (or 3/4) times the
+    column sums of V over the valid keys."""
+    Z, L, H, D = 2, 150, 1, 4
+    nq, nk = [150, 40], [130, 150]
+    rng = np.random.default_rng(81)
+    V = rng.choice([-2.0, -1.5, -1.0, -0.75, -0.5, 0.0, 0.5, 0.75, 1.0, 1.5, 2.0], (Z, L, H, D))
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(V, nq, nk, Z, L, H, D)
+    for b, pw in ((math.log(3.0), 0.75), (math.log(7.0 / 3.0), 11.0 / 16.0)):
+        o = f8a.forward(q8, k8, v8, sq, sk, sv, nq, nk, 0.3, b)
+        for z in range(Z):
+            want = pw * V[z, : nk[z]].sum(axis=0)
+            _close(o[z, : nq[z]], np.broadcast_to(want, (nq[z], H, D)), rtol=0, atol=1e-12, what=f"fp8 O, P={pw}")
+            assert not o[z, nq[z]:].any(), "fp8 padded rows not 0"
+
+
+def pin_fp8_p_tiles():
+    """P is scaled per query row and per tile of 64 keys. With q = e_0, keys
+    0-31 at k = 0 and keys 32-99 at k = -13 e_0 (on the E4M3 grid, as is q),
+    alpha = 1 and b = ln 3, keys 0-31 weigh 3/4 and the others
+    p = 1 / (1 + e^13 / 3), about 6.8e-6. Tile 0's scale comes from 3/4
+    (2^-8): p 2^8 is subnormal in E4M3 (below 2^-6) and within half a step of
+    one step 2^-9, so p becomes 2^-17. Tile 1 (keys 64-99) holds p only, with
+    its own scale 2^(floor(log2 p) - 7) = 2^-25: p 2^25 = 227.5 lies between
+    224 and 240 (step 16), nearer 224, so p becomes 224 * 2^-25."""
+    Z, L, H, D = 1, 100, 1, 2
+    alpha, b = 1.0, math.log(3.0)
+    q = np.zeros((Z, L, H, D))
+    q[0, :, 0, 0] = 1.0
+    k = np.zeros((Z, L, H, D))
+    k[0, 32:, 0, 0] = -13.0
+    V = np.zeros((Z, L, H, D))
+    V[0, :, 0, 0] = 1.0
+    V[0, :, 0, 1] = np.arange(L) % 5 - 2.0
+    n = [L]
+    p = 1.0 / (1.0 + math.exp(13.0) / 3.0)
+    assert 0.5 < p * 2.0**17 < 1.5 and math.floor(math.log2(p)) == -18 and 224 < p * 2.0**25 < 232, "assumptions"
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(V, n, n, Z, L, H, D, q, k)
+    _close(f8a.dequantize(k8, sk), k, rtol=0, atol=0, what="k on the grid")
+    o = f8a.forward(q8, k8, v8, sq, sk, sv, n, n, alpha, b)
+    w = np.where(np.arange(L) < 32, 0.75, np.where(np.arange(L) < 64, 2.0**-17, 224 * 2.0**-25))
+    want = (w[:, None] * V[0, :, 0]).sum(axis=0)
+    _close(o[0, 3, 0], want, rtol=0, atol=1e-15, what="fp8 per-tile P scales")
+
+
+def pin_fp8_scaling_and_bound():
+    """Exact laws of the power-of-two scales (V's bytes + 1 doubles O; Q's bytes
+    + 2 with K's - 2 leave O alone), rows equal the whole, and the P
+    quantisation error stays within 2^-4 sum_j P_j |V_j| (E4M3 relative bound;
+    the weights come from the sigmoid oracle on the dequantised inputs) plus
+    the subnormal tail 2^-17 max_j P_j sum_j |V_j|."""
+    Z, L, H, D = 2, 200, 2, 16
+    nq, nk = [200, 90], [150, 200]
+    rng = np.random.default_rng(82)
+    q, k, v = (rng.standard_normal((Z, L, H, D)) for _ in range(3))
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(v, nq, nk, Z, L, H, D, q, k)
+    alpha, b = 0.25, -1.5
+    o = f8a.forward(q8, k8, v8, sq, sk, sv, nq, nk, alpha, b)
+    _close(f8a.forward(q8, k8, v8, sq, sk, sv + 1, nq, nk, alpha, b), 2 * o, rtol=0, atol=0, what="V scale law")
+    _close(f8a.forward(q8, k8, v8, sq + 2, sk - 2, sv, nq, nk, alpha, b), o, rtol=0, atol=0, what="Q/K scale law")
+    rows = np.array([0, 1, 63, 64, 89, 90, 199])
+    _close(f8a.forward_rows(q8, k8, v8, sq, sk, sv, nq, nk, alpha, b, 1, 1, rows), o[1, rows, 1], rtol=0, atol=0,
+           what="fp8 rows")
+    Q, K, V = (f8a.dequantize(c, s) for c, s in ((q8, sq), (k8, sk), (v8, sv)))
+    exact = osa.forward(Q, K, V, nq, nk, alpha, b)
+    spv = osa.forward(Q, K, np.abs(V), nq, nk, alpha, b)            # sum_j P_j |V_j|
+    pmax = osa.forward(Q, K, np.ones_like(V), nq, nk, alpha, b)     # >= max_j P_j
+    sv_abs = np.stack([np.abs(V[z, : nk[z]]).sum(axis=0) for z in range(Z)])[:, None]
+    bound = 2.0**-4 * spv + 2.0**-17 * pmax * sv_abs
+    assert np.all(np.abs(o - exact) <= bound + 1e-15), "P quantisation beyond the E4M3 bound"
+    assert np.max(np.abs(o - exact)) > 0, "P was not quantised at all"
+
+
 ALL_PINS = [
     pin_sigmoid_closed_forms,
     pin_derivative_bound,
@@ -646,4 +807,9 @@ ALL_PINS = [
     pin_softmax_small_blocks,
     pin_softmax_invariants,
     pin_softmax_finite_differences,
+    pin_e4m3_format,
+    pin_fp8_quantize,
+    pin_fp8_forward_closed_forms,
+    pin_fp8_p_tiles,
+    pin_fp8_scaling_and_bound,
 ]

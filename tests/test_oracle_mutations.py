@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle_pins
+from oracle import fp8_attention as f8a
 from oracle import sigmoid_attention as osa
 from oracle import softmax_attention as sma
 
@@ -177,6 +178,44 @@ def _tile_plan_off_by_one(seqlens_q, seqlens_k, L, block_q, block_k):
     return by_q, by_k
 
 
+# ------------------------------------------------------------------ FP8 path mutants
+_orig_quantize_p = f8a.quantize_p
+_orig_dequantize = f8a.dequantize
+_orig_quantize = f8a.quantize
+_orig_e4m3_round = f8a.e4m3_round
+_orig_tile_exponent = f8a.tile_exponent
+
+
+def _round_ties_away(x):
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    step = np.where(a >= 2.0**-6, np.ldexp(1.0, ex - 1 - 3), 2.0**-9)
+    return np.copysign(np.floor(a / step + 0.5) * step, x)
+
+
+def _round_no_subnormals(x):
+    r = _orig_e4m3_round(x)
+    return np.where(np.abs(r) < 2.0**-6, 0.0, r)
+
+
+def _dequantize_tile32(codes, sbytes, tile=64):
+    return _orig_dequantize(codes, sbytes, 32)
+
+
+def _quantize_padding_too(x, seqlens, tile=64):
+    x = np.asarray(x, np.float64)
+    full = np.full(x.shape[0], x.shape[1])
+    return _orig_quantize(x, full, tile)
+
+
+def _fp8_forward_keys_by_nq(q8, k8, v8, sq, sk, sv, seqlens_q, seqlens_k, alpha, bias):
+    return _orig_fp8_forward(q8, k8, v8, sq, sk, sv, seqlens_q, seqlens_q, alpha, bias)
+
+
+_orig_fp8_forward = f8a.forward
+
+
 MUTANTS = {
     "bias dropped": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(kv, float).T)),
     "alpha dropped": ("scores", lambda qv, kv, a, b: (np.asarray(qv, float) @ np.asarray(kv, float).T) + b),
@@ -212,6 +251,15 @@ MUTANTS = {
     "LSE without max": ("sm:head_forward", _sm_forward("LSE without max")),
     "key blocks renormalised": ("sm:_dkdv_by_key_blocks", _sm_dkdv("key blocks renormalised")),
     "dS drops D": ("sm:_dkdv_by_key_blocks", _sm_dkdv("dS drops D")),
+    "P not quantised": ("f8:quantize_p", lambda p, tile=64: np.asarray(p, np.float64)),
+    "P tiles of 32 keys": ("f8:quantize_p", lambda p, tile=64: _orig_quantize_p(p, 32)),
+    "P scaled over the whole row": ("f8:quantize_p", lambda p, tile=64: _orig_quantize_p(p, max(1, np.shape(p)[1]))),
+    "e4m3 ties away from zero": ("f8:e4m3_round", _round_ties_away),
+    "e4m3 flushes subnormals": ("f8:e4m3_round", _round_no_subnormals),
+    "tile scale one binade low": ("f8:tile_exponent", lambda amax: _orig_tile_exponent(amax) + 1),
+    "dequantised by 32-row tiles": ("f8:dequantize", _dequantize_tile32),
+    "padded rows quantised": ("f8:quantize", _quantize_padding_too),
+    "fp8 keys masked with n_q": ("f8:forward", _fp8_forward_keys_by_nq),
 }
 
 
@@ -221,6 +269,8 @@ def test_mutant_is_caught(name, monkeypatch):
     module = osa
     if attr.startswith("sm:"):
         module, attr = sma, attr[3:]
+    elif attr.startswith("f8:"):
+        module, attr = f8a, attr[3:]
     monkeypatch.setattr(module, attr, fn)
     caught = []
     for pin in oracle_pins.ALL_PINS:
