@@ -226,6 +226,37 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
                         int Z, int L, int H, int D, float alpha, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 forward (OCP E4M3 operands on the gfx950 FP8 MFMA), the FP8 direction
+ * the pages leave as future work (rainbus.top summary of arXiv:2604.27124,
+ * "未来方向"; paperlayer.ai summary, section 5), on the sigmoid forward above.
+ *
+ * sigattn_quantize_fp8 turns a bf16 tensor (layout as `layout` says: padded
+ * [Z, L, H, D] with lengths seq, or packed [T, H, D] with offsets seq) into
+ * E4M3 codes x8 (one byte per element, same layout) and one scale byte per
+ * (sample, head, tile of 64 rows counted from the sample's first row):
+ * scales is uint8 [Z, H, ceil(L / 64)]. A tile's scale is 2^E with
+ * E = floor(log2 amax) - 7 over its valid rows (E = 0 for an all-zero tile,
+ * E >= -127), stored as the E8M0 byte E + 127; code = x * 2^-E rounded to
+ * nearest-even E4M3 (it never overflows: |x| 2^-E < 256). Rows past the
+ * length that lie inside the tensor get code 0; padded rows are not read.
+ * Quantise Q and the query lengths, K and V with the key lengths.
+ *
+ * sigattn_fwd_fp8 computes O (bf16, layout of Q) = sigma(alpha Q K^T + b) V on
+ * the dequantised operands, with P quantised per query row and 64-key tile:
+ * 2^e * E4M3(P 2^-e), e = floor(log2 m) - 7, m the tile's largest P over its
+ * valid keys. Both products accumulate in fp32. Padding, bias modes and
+ * lengths as for sigattn_fwd_ex. alpha must be > 0 and L <= 262144.
+ * Errors: as sigattn_fwd_ex, plus SIGATTN_EINVAL for alpha <= 0, L > 262144
+ * or a NULL scale array. Scale arrays need no alignment.
+ */
+int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, int layout,
+                         int Z, int L, int H, int D, void* stream);
+int sigattn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                    const uint8_t* sq, const uint8_t* sk, const uint8_t* sv, void* o,
+                    const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
+                    int Z, int L, int H, int D, float alpha, float bias, void* stream);
+
 /* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
  * backward (any other value) needs for this shape. 0 means none. */
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype);

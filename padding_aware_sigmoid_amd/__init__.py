@@ -31,7 +31,9 @@ from .ops import (  # noqa: F401
     sigattn_bwd_dv,
     sigattn_bwd_varlen,
     sigattn_fwd,
+    sigattn_fwd_fp8,
     sigattn_fwd_varlen,
+    sigattn_quantize_fp8,
     sigattn_softmax_bwd,
     sigattn_softmax_fwd,
     sigattn_tile_config,

@@ -31,6 +31,8 @@ EXPORTED_SYMBOLS = (
     "sigattn_softmax_fwd",
     "sigattn_softmax_bwd",
     "sigattn_softmax_bwd_workspace_size",
+    "sigattn_quantize_fp8",
+    "sigattn_fwd_fp8",
     "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
@@ -81,6 +83,10 @@ def load():
     lib.sigattn_softmax_bwd.restype = i32
     lib.sigattn_softmax_bwd_workspace_size.argtypes = [ctypes.c_longlong, i32]
     lib.sigattn_softmax_bwd_workspace_size.restype = sz
+    lib.sigattn_quantize_fp8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.sigattn_quantize_fp8.restype = i32
+    lib.sigattn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.sigattn_fwd_fp8.restype = i32
     lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

@@ -40,9 +40,16 @@ hipError_t launch_sm_rowstats(int, const void*, const void*, const float*, void*
 template <int D>
 hipError_t launch_sm_bwd_fp32(const void*, const void*, const void*, const void*, const void*, void*, void*, void*,
                               SeqLayout, int, int, float, float, hipStream_t);
+template <int D>
+hipError_t launch_quantize_fp8(const void*, void*, uint8_t*, SeqLayout, int, int, int, hipStream_t);
+template <int D>
+hipError_t launch_fwd_fp8(const void*, const void*, const void*, const uint8_t*, const uint8_t*, const uint8_t*,
+                          void*, SeqLayout, int, int, float, float, hipStream_t);
 }  // namespace sigattn
 
 namespace {
+
+constexpr int kFp8MaxL = 262144;  // the FP8 forward stages one scale byte per 64-key tile in LDS
 
 thread_local char g_last_error[512] = "";
 
@@ -346,6 +353,42 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
                   : sigattn::launch_sm_bwd_fp32<128>(q, k, v, dout, workspace, dq, dk, dv, sl, Z, H, alpha, c1, st);
   }
   return hip_status(e);
+}
+
+int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, int layout, int Z, int L,
+                         int H, int D, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
+  if (rc != 0) return rc;
+  rc = check_common(Z, L, H, D, 1.0f, 0.0f, SIGATTN_BF16, seq, seq);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(x, "x")) || (rc = check_tensor(x8, "x8"))) return rc;
+  if (scales == nullptr) return fail(SIGATTN_EINVAL, "scales is NULL%s");
+  const sigattn::SeqLayout sl{seq, seq, L, layout, 0};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(D == 64 ? sigattn::launch_quantize_fp8<64>(x, x8, scales, sl, Z, H, 0, st)
+                            : sigattn::launch_quantize_fp8<128>(x, x8, scales, sl, Z, H, 0, st));
+}
+
+int sigattn_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* sq, const uint8_t* sk,
+                    const uint8_t* sv, void* o, const int32_t* seq_q, const int32_t* seq_k, int layout,
+                    int bias_mode, int Z, int L, int H, int D, float alpha, float bias, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_modes(layout, bias_mode);
+  if (rc != 0) return rc;
+  if (!(alpha > 0.0f)) return fail(SIGATTN_EINVAL, "the FP8 forward needs alpha > 0%s");
+  rc = check_common(Z, L, H, D, alpha, bias, SIGATTN_BF16, seq_q, seq_k);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if (L > kFp8MaxL) return fail(SIGATTN_EINVAL, "the FP8 forward takes L <= 262144%s");
+  if ((rc = check_tensor(q8, "q8")) || (rc = check_tensor(k8, "k8")) || (rc = check_tensor(v8, "v8")) ||
+      (rc = check_tensor(o, "o")))
+    return rc;
+  if (sq == nullptr || sk == nullptr || sv == nullptr) return fail(SIGATTN_EINVAL, "a scale array is NULL%s");
+  const sigattn::SeqLayout sl{seq_q, seq_k, L, layout, bias_mode};
+  const float c1 = -alpha * kLog2e, c0 = -bias * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(D == 64 ? sigattn::launch_fwd_fp8<64>(q8, k8, v8, sq, sk, sv, o, sl, Z, H, c1, c0, st)
+                            : sigattn::launch_fwd_fp8<128>(q8, k8, v8, sq, sk, sv, o, sl, Z, H, c1, c0, st));
 }
 
 size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype) {

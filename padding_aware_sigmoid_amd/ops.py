@@ -452,3 +452,76 @@ def softmax_attention(q, k, v, seq_q, seq_k, alpha=None, max_len=None):
     differentiated). Padded [Z, L, H, D] with lengths, or packed [T, H, D] with
     offsets and max_len."""
     return SoftmaxAttention.apply(q, k, v, seq_q, seq_k, alpha, max_len)[0]
+
+
+# ------------------------------------------------------------------------------------------ FP8 path
+
+_FP8_TILE = 64
+
+
+def _fp8_layout(x, seq, max_len):
+    """(layout, Z, L, seq tensor) of an FP8-path tensor: padded [Z, L, H, D] with
+    int32[Z] lengths, or packed [T, H, D] with int32[Z + 1] offsets and max_len."""
+    if x.device.type != "cuda":
+        raise ValueError("sigattn tensors must live on a HIP device")
+    if x.dim() == 4:
+        if not x.is_contiguous():
+            raise ValueError("tensors must be contiguous [Z, L, H, D]")
+        return _lib.LAYOUT_PADDED, x.shape[0], x.shape[1], _lengths(seq, x.shape[0], x.device)
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("packed tensors must be contiguous [T, H, D]")
+    if max_len is None:
+        raise ValueError("packed [T, H, D] tensors need max_len")
+    cu = _offsets(seq, x.device)
+    return _lib.LAYOUT_PACKED, cu.numel() - 1, int(max_len), cu
+
+
+def sigattn_quantize_fp8(x, seq, max_len=None, out=None, scales=None):
+    """(codes, scales) of a bf16 tensor: OCP E4M3 codes (uint8, x's layout) and
+    one E8M0 scale byte per (sample, head, 64-row tile), uint8 [Z, H, ceil(L/64)].
+    Wraps sigattn_quantize_fp8. Padded [Z, L, H, D] with lengths, or packed
+    [T, H, D] with offsets and max_len."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("sigattn_quantize_fp8 takes a bfloat16 tensor")
+    layout, Z, L, sq = _fp8_layout(x, seq, max_len)
+    H, D = x.shape[-2], x.shape[-1]
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    nt = -(-L // _FP8_TILE)
+    sc = torch.empty((Z, H, nt), dtype=torch.uint8, device=x.device) if scales is None else scales
+    if codes.shape != x.shape or codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor of x's shape")
+    if sc.shape != (Z, H, nt) or sc.dtype != torch.uint8 or not sc.is_contiguous():
+        raise ValueError(f"scales must be a contiguous uint8 tensor of shape {(Z, H, nt)}")
+    _lib.check(_lib.load().sigattn_quantize_fp8(x.data_ptr(), codes.data_ptr(), sc.data_ptr(), sq.data_ptr(),
+                                                layout, Z, L, H, D, _stream(x.device)))
+    return codes, sc
+
+
+def sigattn_fwd_fp8(q8, k8, v8, sq, sk, sv, seq_q, seq_k, alpha=None, bias=None, out=None, max_len=None,
+                    bias_mode="constant"):
+    """O (bf16) = sigma(alpha Q K^T + b) V on E4M3 operands with per-tile E8M0
+    scales (as sigattn_quantize_fp8 returns them), P quantised per query row and
+    64-key tile. Wraps sigattn_fwd_fp8. alpha defaults to 1/sqrt(D); bias as in
+    sigattn_fwd, with L = max_len for packed tensors."""
+    layout, Z, L, cq = _fp8_layout(q8, seq_q, max_len)
+    _, _, _, ck = _fp8_layout(k8, seq_k, max_len)
+    H, D = q8.shape[-2], q8.shape[-1]
+    for name, t, ref in (("k8", k8, k8), ("v8", v8, k8)):
+        if t.dtype != torch.uint8 or t.shape != ref.shape or t.shape[-2:] != q8.shape[-2:]:
+            raise ValueError(f"{name} must be uint8 codes of k's shape with q's H and D")
+    if q8.dtype != torch.uint8:
+        raise ValueError("q8 must hold uint8 codes")
+    nt = -(-L // _FP8_TILE)
+    for name, t in (("sq", sq), ("sk", sk), ("sv", sv)):
+        if t.shape != (Z, H, nt) or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {(Z, H, nt)}")
+    mode = _bias_mode(bias_mode)
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    bias = default_bias(max(L, 1), mode) if bias is None else float(bias)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    if o.shape != q8.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of q's shape")
+    _lib.check(_lib.load().sigattn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), sq.data_ptr(),
+                                           sk.data_ptr(), sv.data_ptr(), o.data_ptr(), cq.data_ptr(), ck.data_ptr(),
+                                           layout, mode, Z, L, H, D, alpha, bias, _stream(q8.device)))
+    return o

@@ -133,3 +133,21 @@ def test_grid_limit(lib):
     null, f = None, ctypes.c_void_p(16)
     assert lib.sigattn_fwd(f, f, f, f, f, f, 1 << 20, 1 << 16, 1, 64, 1.0, 0.0, 0, null, 0, null, null) == -1
     assert b"too large" in lib.sigattn_last_error()
+
+
+def test_fp8_argument_errors_need_no_gpu(lib):
+    null, f = None, ctypes.c_void_p(16)
+    q, fwd = lib.sigattn_quantize_fp8, lib.sigattn_fwd_fp8
+    assert q(f, f, null, f, 0, 1, 64, 1, 128, null) == -1
+    assert b"scales" in lib.sigattn_last_error()
+    assert q(f, f, f, f, 3, 1, 64, 1, 128, null) == -1
+    assert q(f, f, f, f, 0, 1, 64, 1, 96, null) == -1
+    assert q(null, null, null, null, 0, 0, 64, 1, 128, null) == 0   # empty batch
+    for a in (0.0, -0.5):
+        assert fwd(f, f, f, f, f, f, f, f, f, 0, 0, 1, 64, 1, 128, a, 0.0, null) == -1
+        assert b"alpha > 0" in lib.sigattn_last_error()
+    assert fwd(f, f, f, f, f, f, f, f, f, 0, 0, 1, 262144 + 64, 1, 128, 0.1, 0.0, null) == -1
+    assert b"262144" in lib.sigattn_last_error()
+    assert fwd(f, f, f, null, f, f, f, f, f, 0, 0, 1, 64, 1, 128, 0.1, 0.0, null) == -1
+    assert b"scale" in lib.sigattn_last_error()
+    assert fwd(f, f, f, f, f, f, f, f, f, 0, 5, 1, 64, 1, 128, 0.1, 0.0, null) == -1
