@@ -18,6 +18,9 @@ Definitions:
   sample. The pages report both no padding and 25% padding.
 * `varlen`: the cell-batch workload (71% padded tokens) timed fwd+bwd in the
   padded layout and in the packed layout on the same valid rows.
+* `fp8`: the FP8 forward on the main workload: quantisation of Q, K and V
+  (per-tile E4M3), then the forward on FP8 MFMA, each timed with HIP events;
+  its TFLOP/s against the FP8 dense peak and against the bf16 forward.
 * `softmax`: padding-aware softmax attention fwd+bwd on the main workload,
   with the same FLOP count, timed per call (forward: one kernel; backward:
   row statistics, dK, dV, dQ) with HIP events on the launch stream.
@@ -38,6 +41,7 @@ ROOT = pathlib.Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
 
 
@@ -50,6 +54,8 @@ def parse():
     ap.add_argument("--pad-workload", default="pad25_16k", help="secondary workload reported in the same line ('' to skip)")
     ap.add_argument("--varlen-workload", default="cellbatch8k",
                     help="workload timed in the padded and the packed layout ('none' skips)")
+    ap.add_argument("--fp8-workload", default="nopad16k",
+                    help="workload of the FP8 forward sub-object ('' to skip)")
     ap.add_argument("--softmax-workload", default="nopad16k",
                     help="workload of the softmax fwd+bwd sub-object ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -190,6 +196,57 @@ def run_layouts(name, steps, warmup, seed=0):
         out[f"{label}_tflops_valid"] = round(fl["total_valid"] / (ms * 1e-3) / 1e12, 2)
     out["packed_speedup"] = round(res["padded"] / res["packed"], 3)
     del q, k, v, do, qp, kp, vp, dop, o, dq, dk, dv, op, dqp, dkp, dvp
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_fp8(name, steps, warmup, seed=0):
+    """FP8 forward on one workload: quantisation of Q, K, V and the forward,
+    each timed per call with HIP events on the launch stream."""
+    import torch
+
+    import padding_aware_sigmoid_amd as sa
+    import workloads
+    from padding_aware_sigmoid_amd import accounting
+
+    inp = workloads.make_inputs(name, seed=seed)
+    w = inp["workload"]
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    nq = torch.as_tensor(inp["seqlens_q"]).to(dev)
+    nk = torch.as_tensor(inp["seqlens_k"]).to(dev)
+    q8, sq = sa.sigattn_quantize_fp8(q, nq)
+    k8, sk = sa.sigattn_quantize_fp8(k, nk)
+    v8, sv = sa.sigattn_quantize_fp8(v, nk)
+    o8 = torch.empty_like(q)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    calls = [
+        lambda: (sa.sigattn_quantize_fp8(q, nq, out=q8, scales=sq), sa.sigattn_quantize_fp8(k, nk, out=k8, scales=sk),
+                 sa.sigattn_quantize_fp8(v, nk, out=v8, scales=sv)),
+        lambda: sa.sigattn_fwd_fp8(q8, k8, v8, sq, sk, sv, nq, nk, w.alpha, w.bias, out=o8),
+        lambda: sa.sigattn_fwd(q, k, v, nq, nk, w.alpha, w.bias, out=o),
+    ]
+    for _ in range(warmup):
+        for fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        for i, fn in enumerate(calls):
+            e[i].record(stream)
+            fn()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(3)]
+    fl = accounting.attention_flops(w.Z, w.L, w.H, w.D, inp["seqlens_q"], inp["seqlens_k"])
+    tf = fl["fwd_valid"] / (t[1] * 1e-3) / 1e12
+    diff = float((o8.float() - o.float()).abs().max() / o.float().abs().max())
+    out = {"workload": w.name, "Z": w.Z, "H": w.H, "L": w.L, "D": w.D, "format": "OCP E4M3, per-tile E8M0 scales",
+           "quantize_qkv_ms": round(t[0], 4), "fwd_ms": round(t[1], 4), "fwd_tflops_valid": round(tf, 2),
+           "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "bf16_fwd_ms": round(t[2], 4),
+           "speedup_vs_bf16_fwd": round(t[2] / t[1], 3), "max_rel_diff_vs_bf16_fwd": round(diff, 4)}
+    del q, k, v, q8, k8, v8, o8, o
     torch.cuda.empty_cache()
     return out
 
@@ -343,6 +400,8 @@ def main():
         }
     if args.varlen_workload not in ("", "none"):
         line["varlen"] = run_layouts(args.varlen_workload, args.steps, args.warmup)
+    if args.fp8_workload not in ("", "none"):
+        line["fp8"] = run_fp8(args.fp8_workload, args.steps, args.warmup)
     if args.softmax_workload not in ("", "none"):
         sm = run_softmax(args.softmax_workload, args.steps, args.warmup)
         if args.softmax_workload == args.workload:

@@ -30,9 +30,8 @@
 //    t+1 on the MFMAs beside sigma of tile t, then P V of tile t beside the
 //    masking and scale of tile t+1.
 //  - LDS rows are D bytes of 16-byte chunks, chunk c of row r stored at
-//    c ^ ((r / (256 / D)) mod (D / 16)): the row reads of K (32 lanes, 32
-//    consecutive rows, one chunk) and the transposed reads of V
-//    (ds_read_b64_tr_b8: 8 rows, one chunk) are free of bank conflicts.
+//    c ^ f8_swz(r): the row reads of K and the transposed reads of V
+//    (ds_read_b64_tr_b8) are free of bank conflicts.
 //  - Keys at or past n_k are read as zero rows and masked to -inf before the
 //    tile maximum, so their weight is exactly 0 and P's scale comes from valid
 //    keys only.
@@ -60,9 +59,25 @@ constexpr int kE8M0One = 127; // E8M0 byte of 2^0
 // Key tiles per sample whose scale bytes the forward stages in LDS: L <= 262144.
 constexpr int kF8MaxTiles = 4096;
 
+// LDS bank groups (16 bytes) of chunk c of row r are spread by an XOR of c
+// with f8_swz(r). LDS serves 16 lanes of 16-byte reads (or 32 lanes of 8-byte
+// reads) per 256-byte phase. D = 128: rows are 128 bytes, two per phase; the
+// K row reads (16 consecutive rows, one chunk) and the transposed V reads
+// (rows {0-3, 8-11} + 4h, two adjacent chunks) each hit 16 distinct groups.
+// D = 64: rows are 64 bytes, four per phase.
+template <int D>
+__device__ __forceinline__ int f8_swz(int r) {
+  if constexpr (D == 128) {
+    const int k = (r >> 1) & 7;
+    return ((k & 1) << 2) | (k >> 1);
+  } else {
+    return (r >> 2) & 3;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ int f8_off(int r, int c) {
-  return r * D + ((c ^ ((r / (256 / D)) & (D / 16 - 1))) << 4);
+  return r * D + ((c ^ f8_swz<D>(r)) << 4);
 }
 
 // One 32-byte MFMA operand: chunks c and c + 1 of row r.
@@ -113,7 +128,7 @@ __device__ __forceinline__ void dma_tile8(uint8_t* tile, const uint8_t* rows, ui
     const int P0 = i * 256 + wbase;
     const int P = P0 + lane;
     const int r = P / CPR, cs = P % CPR;
-    const int c = cs ^ ((r / (256 / D)) & (CPR - 1));
+    const int c = cs ^ f8_swz<D>(r);
     const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
     llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16),
                                     16, (int)voff, 0, 0, 0);

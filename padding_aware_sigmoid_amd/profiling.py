@@ -42,7 +42,8 @@ def kernel_source_hash() -> str:
 def short_name(kernel: str) -> str | None:
     """The bench name of a sigattn kernel from its demangled or mangled name,
     else None. Sigmoid bf16: fwd, dq, dk, dv, dkdv; softmax: the same with an
-    sm_ prefix, plus sm_rowstats; fp32 kernels carry a _fp32 suffix."""
+    sm_ prefix, plus sm_rowstats; fp32 kernels carry a _fp32 suffix; the FP8
+    path's kernels are fp8_fwd and fp8_quantize."""
     m = re.search(r"sigattn::(\w+?)_kernel<([^>]*)>", kernel)
     if m is not None:
         base, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
@@ -59,6 +60,8 @@ def short_name(kernel: str) -> str | None:
     core = base[3:] if sm else base
     if core == "rowstats":
         return "sm_rowstats" + ("_fp32" if float_arg else "")
+    if core in ("fwd_fp8", "quantize_fp8"):
+        return "fp8_" + core.split("_")[0]
     mk = re.fullmatch(r"(fwd|dq|dkdv)_(bf16|fp32)", core)
     if mk is None:
         return None

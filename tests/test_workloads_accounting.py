@@ -89,6 +89,9 @@ def test_profile_kernel_names():
         "_ZN7sigattn14dq_bf16_kernelILi128ELi0EEEvPKDF16b": "dq",
         "_ZN7sigattn18sm_rowstats_kernelIDF16bLi128EEEvPKT_": "sm_rowstats",
         "_ZN7sigattn18sm_fwd_bf16_kernelILi64EEEvPKDF16b": "sm_fwd",
+        "void sigattn::fwd_fp8_kernel<128>(...)": "fp8_fwd",
+        "void sigattn::quantize_fp8_kernel<64>(...)": "fp8_quantize",
+        "_ZN7sigattn14fwd_fp8_kernelILi128EEEvPKhS2_S2_S2_S2_S2_PDF16b": "fp8_fwd",
         "__amd_rocclr_copyBuffer": None,
     }
     for name, want in cases.items():
