@@ -27,8 +27,11 @@ AGPR_FORM_SOURCES = {"bwd_softmax_dk128.hip"}
 # (valid inputs are finite; padded rows are never read) each fmaxf is one
 # v_max_f32 instead of two (no quieting of NaN inputs): 46 fewer VALU
 # instructions per key tile. Infinities keep their meaning (masked keys are -inf).
+# Machine sinking would move sigma and the P V MFMAs of a tile past the branch
+# that masks the last tile, out of the block whose schedule interleaves them
+# with the score MFMAs; without it each tile's work stays in one block.
 EXTRA_FLAGS = {"bwd_softmax_dk128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-               "fp8.hip": ["-fno-honor-nans"]}
+               "fp8.hip": ["-fno-honor-nans", "-mllvm", "-disable-machine-sink"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
