@@ -368,18 +368,25 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
       const uint8_t* vt = vx;
       i32x8 p8[2];
       float pw[4];
-      i32x8 a_op;
+      // Every LDS operand of the tile is requested up front: K(t+1) for the S
+      // phase and V(t)^T for the P V phase, so no MFMA waits on a read.
+      i32x8 a_ops[2][C::KS], b_ops[C::NB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) a_ops[kb][s] = lds8_row<D>(kt, 32 * kb + l32, 4 * s + 2 * half);
+#pragma unroll
+      for (int db = 0; db < C::NB; ++db) b_ops[db] = lds8_vt<D>(vt, db, lane);
       static_for<0, NS>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         constexpr int kb = g / (2 * C::KS), s = (g / 2) % C::KS, qb = g % 2;
-        if constexpr (qb == 0) a_op = lds8_row<D>(kt, 32 * kb + l32, 4 * s + 2 * half);
         if constexpr (s == 0) {
           f32x16 z;
 #pragma unroll
           for (int r = 0; r < 16; ++r) z[r] = 0.0f;
-          sn[kb][qb] = mfma8(a_op, qf[qb][s], z, skb, sq_byte);
+          sn[kb][qb] = mfma8(a_ops[kb][s], qf[qb][s], z, skb, sq_byte);
         } else {
-          sn[kb][qb] = mfma8(a_op, qf[qb][s], sn[kb][qb], skb, sq_byte);
+          sn[kb][qb] = mfma8(a_ops[kb][s], qf[qb][s], sn[kb][qb], skb, sq_byte);
         }
         constexpr int e0 = g * 64 / NS, e1 = (g + 1) * 64 / NS;
         static_for<e0, e1>([&](auto ec) {
@@ -390,16 +397,14 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
             p8[eq][j] = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3],
                                                         __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], 0, false), true);
         });
-        sched_step<g, (qb == 0 ? 2 : 0), 1, (e1 - e0) * 9 / 2, kNoFence>();
+        sched_step<g, 0, 1, (e1 - e0) * 9 / 2, kNoFence>();
       });
       __builtin_amdgcn_sched_barrier(0);
-      i32x8 b_op;
       static_for<0, NP>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         constexpr int db = g / 2, qb = g % 2;
-        if constexpr (qb == 0) b_op = lds8_vt<D>(vt, db, lane);
-        oacc[qb][db] = mfma8(p8[qb], b_op, oacc[qb][db], pbyte[qb], svb);
-        sched_step<g, (qb == 0 ? 4 : 0), 1, 8, kNoFence>();
+        oacc[qb][db] = mfma8(p8[qb], b_ops[db], oacc[qb][db], pbyte[qb], svb);
+        sched_step<g, 0, 1, 8, kNoFence>();
       });
       mask_and_scale(sn, (t + 1) * C::BK);
     };
