@@ -345,17 +345,21 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
       }
     });
     constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
-    sched_step<j, nds, 2, (e1 - e0) * (DK ? 7 : 5), kNoFence>();  // a hard fence makes the dK kernel spill
+    // A hard fence every second step keeps the dV kernel's LDS reads two
+    // steps ahead of their MFMAs. In the kernels that compute dK it makes the
+    // compiler spill or fail, so they schedule each kv_step as one region.
+    constexpr int FENCE = MODE == KV_DV ? 2 : kNoFence;
+    sched_step<j, nds, 2, (e1 - e0) * (DK ? 7 : 5), FENCE>();
   });
 }
 
 // Whether the dK/dV query loop is unrolled over the three ring slots. Unrolled,
 // every LDS access names its slot at compile time, and the compiler does not
-// wait for the DMA into one slot before reading the others. That costs a few
-// registers (slot addresses past the 64 KB read offset range need their own),
-// which the two kernels already at the register limit (fused dK+dV at D = 64,
-// dK at D = 128) cannot spare: they keep a runtime slot index, and the compiler
-// waits for each DMA before their next LDS read.
+// wait for the DMA into one slot before reading the others. The two kernels
+// already at the register limit (fused dK+dV at D = 64, dK at D = 128) spill
+// heavily when unrolled. They keep a runtime slot index into one array, with
+// the DMA destinations hidden from the compiler (lds_opaque), which then
+// does not wait for a DMA before their next LDS read either.
 template <int D, int MODE>
 constexpr bool kUnrolledRing = !(MODE == KV_BOTH || (MODE == KV_DK && D == 128));
 
@@ -372,15 +376,19 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   using C = BwdCfg<D>;
   constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   constexpr bool SM = ACT == ACT_SOFTMAX;
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sG2[C::TILE];
-  __shared__ __attribute__((aligned(64))) float2 sS0[SM ? 64 : 1];
-  __shared__ __attribute__((aligned(64))) float2 sS1[SM ? 64 : 1];
-  __shared__ __attribute__((aligned(64))) float2 sS2[SM ? 64 : 1];
+  constexpr bool UR = kUnrolledRing<D, MODE>;
+  constexpr int TS = UR ? C::TILE : 8;  // the runtime-indexed ring lives in sRing instead
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[TS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[TS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ2[TS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG0[TS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG1[TS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sG2[TS];
+  __shared__ __attribute__((aligned(64))) float2 sS0[SM && UR ? 64 : 1];
+  __shared__ __attribute__((aligned(64))) float2 sS1[SM && UR ? 64 : 1];
+  __shared__ __attribute__((aligned(64))) float2 sS2[SM && UR ? 64 : 1];
+  __shared__ __attribute__((aligned(1024))) __bf16 sRing[UR ? 8 : 6 * C::TILE];
+  __shared__ __attribute__((aligned(64))) float2 sSRing[SM && !UR ? 3 * 64 : 1];
   __shared__ int rank_lds[kMaxRankedSamples];
   const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;
   const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, sl, rank_lds);
@@ -457,15 +465,17 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
       kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
                                               ptX, dsX, sX, pX, kf, vf, c1, c0, s_cur, l32, half, lane);
     };
-    auto prologue = [&](int n_tiles) {
-      fetch(sQ0, sG0, sS0, 0);
+    // Tile 0 into slot 0, then tile 1 into slot 1 (q1, g1, s1: its DMA
+    // destinations) behind the first A stages.
+    auto prologue = [&](__bf16* q0, __bf16* g0, float2* s0, __bf16* q1, __bf16* g1, float2* s1, int n_tiles) {
+      fetch(q0, g0, s0, 0);
       dma_wait();
       __syncthreads();
-      if (n_tiles > 1) fetch(sQ1, sG1, sS1, 1);  // no DMA may be left in flight when the kernel ends
-      kv_step<D, MODE, ACT, true, false, false>(sQ0, sG0, 0, sQ0, sG0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY,
-                                                sY, pY, kf, vf, c1, c0, sS0, l32, half, lane);
-      kv_step<D, MODE, ACT, true, false, true>(sQ0, sG0, 1, sQ0, sG0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX,
-                                               sX, pX, kf, vf, c1, c0, sS0, l32, half, lane);
+      if (n_tiles > 1) fetch(q1, g1, s1, 1);  // no DMA may be left in flight when the kernel ends
+      kv_step<D, MODE, ACT, true, false, false>(q0, g0, 0, q0, g0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
+                                                pY, kf, vf, c1, c0, s0, l32, half, lane);
+      kv_step<D, MODE, ACT, true, false, true>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
+                                               pX, kf, vf, c1, c0, s0, l32, half, lane);
     };
     auto epilogue = [&](__bf16* q_last, __bf16* g_last, float2* s_last) {
       kv_step<D, MODE, ACT, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
       // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
       // exactly nothing to dV or dK.
       const int nqt3 = 1 + (nqt + 1) / 3 * 3;
-      prologue(nqt3);
+      prologue(sQ0, sG0, sS0, sQ1, sG1, sS1, nqt3);
       for (int u = 1; u < nqt3; u += 3) {
         iteration(sQ1, sG1, sS1, sQ0, sG0, sQ2, sG2, sS2, u, nqt3);
         iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt3);
@@ -486,17 +496,23 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
       }
       epilogue(sQ0, sG0, sS0);  // tile nqt3 - 1 sits in slot 0
     } else {
-      auto q_at = [&](int i) { return i == 0 ? sQ0 : (i == 1 ? sQ1 : sQ2); };
-      auto g_at = [&](int i) { return i == 0 ? sG0 : (i == 1 ? sG1 : sG2); };
-      auto s_at = [&](int i) { return i == 0 ? sS0 : (i == 1 ? sS1 : sS2); };
-      prologue(nqt);
+      // The three slots are parts of one array, indexed at run time. Every
+      // read names that array, so the compiler can match it against DMAs.
+      // The DMA destinations are passed through lds_opaque: the compiler does
+      // not match the reads against them and inserts no wait for the DMA in
+      // flight. The DMA of a tile is waited for explicitly (dma_wait and the
+      // barrier at the top of the next iteration) before any read of it.
+      auto q_at = [&](int i) { return sRing + (2 * i) * C::TILE; };
+      auto g_at = [&](int i) { return sRing + (2 * i + 1) * C::TILE; };
+      auto s_at = [&](int i) { return SM ? sSRing + 64 * i : sSRing; };
+      prologue(q_at(0), g_at(0), s_at(0), lds_opaque(q_at(1)), lds_opaque(g_at(1)), lds_opaque(s_at(1)), nqt);
       int cur = 0;
       for (int u = 1; u < nqt; ++u) {
         const int prev = cur;
         cur = (cur == 2) ? 0 : cur + 1;
         const int next = (cur == 2) ? 0 : cur + 1;
-        iteration(q_at(cur), g_at(cur), s_at(cur), q_at(prev), g_at(prev), q_at(next), g_at(next), s_at(next), u,
-                  nqt);
+        iteration(q_at(cur), g_at(cur), s_at(cur), q_at(prev), g_at(prev), lds_opaque(q_at(next)),
+                  lds_opaque(g_at(next)), lds_opaque(s_at(next)), u, nqt);
       }
       epilogue(q_at(cur), g_at(cur), s_at(cur));
     }

@@ -379,6 +379,19 @@ __device__ __forceinline__ void dma_stats64(float2* dst, const float2* src, uint
                                   (int)voff, 0, 0, 0);
 }
 
+// The same LDS address, with no link to the array it points into that the
+// compiler can follow. A DMA into such an address does not make the compiler
+// wait for it before reads of that array; the kernel orders the two itself
+// (dma_wait, then a barrier, before any read of the DMA's destination). The
+// address is workgroup-uniform.
+template <typename T>
+__device__ __forceinline__ T* lds_opaque(T* p) {
+  typedef __attribute__((address_space(3))) char* lds_char_ptr;
+  uint32_t a = (uint32_t)(size_t)(lds_char_ptr)p;
+  asm volatile("" : "+s"(a));
+  return (T*)(lds_char_ptr)(size_t)a;
+}
+
 // Wait until this wave's outstanding global loads (the DMAs included) are done.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
