@@ -226,7 +226,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
-// Wave w owns 64 key rows (two 32-row blocks). It holds K and V as B operands, for:
+// Wave w owns KB 32-row key blocks (KB = 2, 64 keys, except the fused form at
+// D = 128: KB = 1). It holds K and V as B operands, for:
 //   S  = Q K^T   (A = Q from LDS)
 //   dP = dO V^T  (A = dO from LDS)
 // P^T and dS^T come straight from those accumulators as A operands, for:
@@ -243,22 +244,28 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 //   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
 //   KV_DK (S, dP, dK: 6*D) and KV_DV (S, dV: 4*D) split the work over two
 //   launches.
-// At D = 128 the K and V operands plus both accumulators do not fit one
-// wave's registers (the fused form spills), so D = 128 runs the split form.
+// At D = 128 the K and V operands plus both accumulators for 64 keys do not
+// fit one wave's registers, so the fused form there gives each wave 32 keys
+// (KB = 1) and runs the workgroup's 256 keys as two halves of 128, each
+// streaming all query tiles. The split forms keep KB = 2.
 enum KvMode { KV_BOTH = 0, KV_DK = 1, KV_DV = 2 };
+
+// Key blocks of 32 rows per wave.
+template <int D, int MODE>
+constexpr int kKB = (D == 128 && MODE == KV_BOTH) ? 1 : 2;
 
 // stA (softmax only): the row statistics {LSE / alpha, D} of the tile whose
 // query block qba the A stage processes. The A stage starts its accumulators
 // at -LSE / alpha and -D instead of 0, so its MFMAs leave s' = s - LSE / alpha
 // and dP' = dP - D, and the V stage needs no statistics: P = 2^(c1 s') and
 // dS = P dP'.
-template <int D, int MODE, int ACT, bool DO_A, bool DO_B, bool DO_V>
+template <int D, int MODE, int ACT, bool DO_A, bool DO_B, bool DO_V, int KB = kKB<D, MODE>>
 __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, int qba, const __bf16* sQb,
-                                        const __bf16* sGb, int qbb, f32x16 (&sN)[2], f32x16 (&pN)[2],
-                                        f32x16 (&dkacc)[2][BwdCfg<D>::NB], f32x16 (&dvacc)[2][BwdCfg<D>::NB],
-                                        const bf16x8 (&ptB)[2][2], const bf16x8 (&dsB)[2][2], bf16x8 (&ptV)[2][2],
-                                        bf16x8 (&dsV)[2][2], const f32x16 (&sV)[2], const f32x16 (&pV)[2],
-                                        const bf16x8 (&kf)[2][BwdCfg<D>::KS], const bf16x8 (&vf)[2][BwdCfg<D>::KS],
+                                        const __bf16* sGb, int qbb, f32x16 (&sN)[KB], f32x16 (&pN)[KB],
+                                        f32x16 (&dkacc)[KB][BwdCfg<D>::NB], f32x16 (&dvacc)[KB][BwdCfg<D>::NB],
+                                        const bf16x8 (&ptB)[KB][2], const bf16x8 (&dsB)[KB][2], bf16x8 (&ptV)[KB][2],
+                                        bf16x8 (&dsV)[KB][2], const f32x16 (&sV)[KB], const f32x16 (&pV)[KB],
+                                        const bf16x8 (&kf)[KB][BwdCfg<D>::KS], const bf16x8 (&vf)[KB][BwdCfg<D>::KS],
                                         float c1, float c0, const float2* stA, int l32, int half, int lane) {
   using C = BwdCfg<D>;
   constexpr bool DK = MODE != KV_DV, DV = MODE != KV_DK;
@@ -266,7 +273,7 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
   constexpr int PB = (DK ? 1 : 0) + (DV ? 1 : 0);  // B operands per (db, ks): dO tr (dV), Q tr (dK)
   constexpr int NA = DO_A ? PA * C::KS : 0;
   constexpr int NSTEP = NA + (DO_B ? PB * 2 * C::NB : 0);
-  constexpr int NV = DO_V ? 32 : 0;
+  constexpr int NV = DO_V ? 16 * KB : 0;
   // which job operand j belongs to: 0 = Q nat, 1 = dO nat, 2 = dO tr, 3 = Q tr
   auto kind = [](int j) constexpr -> int {
     if (j < NA) return (PA == 2 && (j & 1)) ? 1 : 0;
@@ -286,10 +293,12 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
   };
   if constexpr (DO_A && ACT == ACT_SIGMOID) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sN[0][r] = sN[1][r] = 0.0f;
-      if constexpr (DK) pN[0][r] = pN[1][r] = 0.0f;
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sN[kb][r] = 0.0f;
+        if constexpr (DK) pN[kb][r] = 0.0f;
+      }
   } else if constexpr (DO_A) {
     // Register r holds row (r/4)*8 + 4*half + r%4 of the block: 4 groups of 4 rows.
 #pragma unroll
@@ -298,10 +307,12 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
       const float4 a = src[0], b = src[1];
       const float l[4] = {a.x, a.z, b.x, b.z}, d[4] = {a.y, a.w, b.y, b.w};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        sN[0][4 * g + rr] = sN[1][4 * g + rr] = -l[rr];
-        if constexpr (DK) pN[0][4 * g + rr] = pN[1][4 * g + rr] = -d[rr];
-      }
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sN[kb][4 * g + rr] = -l[rr];
+          if constexpr (DK) pN[kb][4 * g + rr] = -d[rr];
+        }
     }
   }
   bf16x8 ops[3];
@@ -312,22 +323,18 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
     constexpr int k = kind(j);
     if constexpr (j + 2 < NSTEP) ops[(j + 2) % 3] = read(std::integral_constant<int, j + 2>{});
     const bf16x8 op = ops[j % 3];
-    if constexpr (k == 0) {
-      constexpr int s = j / PA;
-      sN[0] = mfma32(op, kf[0][s], sN[0]);
-      sN[1] = mfma32(op, kf[1][s], sN[1]);
-    } else if constexpr (k == 1) {
-      constexpr int s = j / PA;
-      pN[0] = mfma32(op, vf[0][s], pN[0]);
-      pN[1] = mfma32(op, vf[1][s], pN[1]);
-    } else {
-      constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
-      if constexpr (k == 2) {
-        dvacc[0][db] = mfma32(ptB[0][ks], op, dvacc[0][db]);
-        dvacc[1][db] = mfma32(ptB[1][ks], op, dvacc[1][db]);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (k == 0) {
+        sN[kb] = mfma32(op, kf[kb][j / PA], sN[kb]);
+      } else if constexpr (k == 1) {
+        pN[kb] = mfma32(op, vf[kb][j / PA], pN[kb]);
       } else {
-        dkacc[0][db] = mfma32(dsB[0][ks], op, dkacc[0][db]);
-        dkacc[1][db] = mfma32(dsB[1][ks], op, dkacc[1][db]);
+        constexpr int i = (j - NA) / PB, db = i >> 1, ks = i & 1;
+        if constexpr (k == 2)
+          dvacc[kb][db] = mfma32(ptB[kb][ks], op, dvacc[kb][db]);
+        else
+          dkacc[kb][db] = mfma32(dsB[kb][ks], op, dkacc[kb][db]);
       }
     }
     constexpr int e0 = j * NV / NSTEP, e1 = (j + 1) * NV / NSTEP;
@@ -345,11 +352,12 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
       }
     });
     constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
-    // A hard fence every second step keeps the dV kernel's LDS reads two
-    // steps ahead of their MFMAs. In the kernels that compute dK it makes the
-    // compiler spill or fail, so they schedule each kv_step as one region.
-    constexpr int FENCE = MODE == KV_DV ? 2 : kNoFence;
-    sched_step<j, nds, 2, (e1 - e0) * (DK ? 7 : 5), FENCE>();
+    // A hard fence every second step keeps the LDS reads two steps ahead of
+    // their MFMAs (the dV kernel, and the fused form with one key block). In
+    // the other kernels that compute dK it makes the compiler spill or fail,
+    // so they schedule each kv_step as one region.
+    constexpr int FENCE = (MODE == KV_DV || KB == 1) ? 2 : kNoFence;
+    sched_step<j, nds, KB, (e1 - e0) * (DK ? 7 : 5), FENCE>();
   });
 }
 
@@ -361,7 +369,7 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
 // the DMA destinations hidden from the compiler (lds_opaque), which then
 // does not wait for a DMA before their next LDS read either.
 template <int D, int MODE>
-constexpr bool kUnrolledRing = !(MODE == KV_BOTH || (MODE == KV_DK && D == 128));
+constexpr bool kUnrolledRing = !((MODE == KV_BOTH && D == 64) || (MODE == KV_DK && D == 128));
 
 // One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV), for the
 // attention ACT selects. With softmax each query tile's row statistics
@@ -417,119 +425,141 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
     return;
   }
 
-  bf16x8 kf[2][C::KS], vf[2][C::KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int kr = k0 + 64 * w + 32 * kb + l32;
-    const bool ok = kr < nk;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      kf[kb][s] = ok ? *(const bf16x8*)(K + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
-      if (DO_DK) vf[kb][s] = ok ? *(const bf16x8*)(V + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
-    }
-  }
-  f32x16 dkacc[2][C::NB], dvacc[2][C::NB];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dkacc[kb][db][r] = dvacc[kb][db][r] = 0.0f;
-
+  constexpr int KB = kKB<D, MODE>;
+  constexpr int WK = 32 * KB;           // keys per wave
+  constexpr int SUB = C::NWAVE * WK;    // keys per pass over the queries
   const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
-  if (nqt > 0) {
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const __bf16* Qb = Q + base_q;
-    const __bf16* dOb = dO + base_q;
-    const float2* Sb = SM ? stats + sl.row0_q(z) * H + h : nullptr;
-    auto fetch = [&](__bf16* sq, __bf16* sg, float2* ss, int tile) {
-      const int r0 = tile * C::BQ_KV;
-      const size_t off = (size_t)(r0 < nq ? r0 : 0) * rs;  // no row is read past n_q
-      dma_tile<D, 64, 256>(sq, Qb + off, row_bytes, nq - r0, tid);
-      dma_tile<D, 64, 256>(sg, dOb + off, row_bytes, nq - r0, tid);
-      if constexpr (SM) dma_stats64(ss, Sb + (size_t)(r0 < nq ? r0 : 0) * H, (uint32_t)(H * 8), nq - r0, tid);
-    };
-    f32x16 sX[2], pX[2], sY[2], pY[2];
-    bf16x8 ptX[2][2], ptY[2][2], dsX[2][2], dsY[2][2];
-    // Query tile u: its slot (q_cur, g_cur), tile u-1's slot (q_prev, g_prev)
-    // and the slot that receives tile u+1 (it held tile u-2).
-    // The V stage of each step turns the previous A stage's block into P (and
-    // dS). The A stage reads the row statistics of its own tile (s_cur).
-    auto iteration = [&](__bf16* q_cur, __bf16* g_cur, float2* s_cur, __bf16* q_prev, __bf16* g_prev,
-                         __bf16* q_next, __bf16* g_next, float2* s_next, int u, int n_tiles) {
-      dma_wait();
-      __syncthreads();
-      if (u + 1 < n_tiles) fetch(q_next, g_next, s_next, u + 1);
-      kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX,
-                                              ptY, dsY, sY, pY, kf, vf, c1, c0, s_cur, l32, half, lane);
-      kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
-                                              ptX, dsX, sX, pX, kf, vf, c1, c0, s_cur, l32, half, lane);
-    };
-    // Tile 0 into slot 0, then tile 1 into slot 1 (q1, g1, s1: its DMA
-    // destinations) behind the first A stages.
-    auto prologue = [&](__bf16* q0, __bf16* g0, float2* s0, __bf16* q1, __bf16* g1, float2* s1, int n_tiles) {
-      fetch(q0, g0, s0, 0);
-      dma_wait();
-      __syncthreads();
-      if (n_tiles > 1) fetch(q1, g1, s1, 1);  // no DMA may be left in flight when the kernel ends
-      kv_step<D, MODE, ACT, true, false, false>(q0, g0, 0, q0, g0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
-                                                pY, kf, vf, c1, c0, s0, l32, half, lane);
-      kv_step<D, MODE, ACT, true, false, true>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
-                                               pX, kf, vf, c1, c0, s0, l32, half, lane);
-    };
-    auto epilogue = [&](__bf16* q_last, __bf16* g_last, float2* s_last) {
-      kv_step<D, MODE, ACT, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
-                                               dsX, ptY, dsY, sY, pY, kf, vf, c1, c0, s_last, l32, half, lane);
-      kv_step<D, MODE, ACT, false, true, false>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY,
-                                                dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, s_last, l32, half, lane);
-    };
-    if constexpr (kUnrolledRing<D, MODE>) {
-      // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
-      // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
-      // exactly nothing to dV or dK.
-      const int nqt3 = 1 + (nqt + 1) / 3 * 3;
-      prologue(sQ0, sG0, sS0, sQ1, sG1, sS1, nqt3);
-      for (int u = 1; u < nqt3; u += 3) {
-        iteration(sQ1, sG1, sS1, sQ0, sG0, sQ2, sG2, sS2, u, nqt3);
-        iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt3);
-        iteration(sQ0, sG0, sS0, sQ2, sG2, sQ1, sG1, sS1, u + 2, nqt3);
-      }
-      epilogue(sQ0, sG0, sS0);  // tile nqt3 - 1 sits in slot 0
-    } else {
-      // The three slots are parts of one array, indexed at run time. Every
-      // read names that array, so the compiler can match it against DMAs.
-      // The DMA destinations are passed through lds_opaque: the compiler does
-      // not match the reads against them and inserts no wait for the DMA in
-      // flight. The DMA of a tile is waited for explicitly (dma_wait and the
-      // barrier at the top of the next iteration) before any read of it.
-      auto q_at = [&](int i) { return sRing + (2 * i) * C::TILE; };
-      auto g_at = [&](int i) { return sRing + (2 * i + 1) * C::TILE; };
-      auto s_at = [&](int i) { return SM ? sSRing + 64 * i : sSRing; };
-      prologue(q_at(0), g_at(0), s_at(0), lds_opaque(q_at(1)), lds_opaque(g_at(1)), lds_opaque(s_at(1)), nqt);
-      int cur = 0;
-      for (int u = 1; u < nqt; ++u) {
-        const int prev = cur;
-        cur = (cur == 2) ? 0 : cur + 1;
-        const int next = (cur == 2) ? 0 : cur + 1;
-        iteration(q_at(cur), g_at(cur), s_at(cur), q_at(prev), g_at(prev), lds_opaque(q_at(next)),
-                  lds_opaque(g_at(next)), lds_opaque(s_at(next)), u, nqt);
-      }
-      epilogue(q_at(cur), g_at(cur), s_at(cur));
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::NB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = k0 + 64 * w + 32 * kb + acc_row(r, half);
-        if (row < rows) {
-          const bool ok = row < nk;
-          if (DO_DK) dKb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? alpha * dkacc[kb][db][r] : 0.0f);
-          if (DO_DV) dVb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? dvacc[kb][db][r] : 0.0f);
+  constexpr int NPASS = C::BK_KV / SUB;
+  // One pass over the query tiles per SUB keys (two passes when KB = 1). A
+  // second pass that lies wholly in padding only writes its zero rows.
+  for (int ip = 0; ip < NPASS; ++ip) {
+    const int kh = k0 + ip * SUB;
+    if constexpr (NPASS > 1) {
+      if (kh >= nk) {
+        const int rows_here = min(SUB, rows - kh);
+        const bf16x8 zz = zero_bf16x8();
+        for (int c = tid; c < rows_here * (D / 8); c += 256) {
+          const size_t off = (size_t)(kh + c / (D / 8)) * rs + (c % (D / 8)) * 8;
+          if (DO_DK) *(bf16x8*)(dKb + off) = zz;
+          if (DO_DV) *(bf16x8*)(dVb + off) = zz;
         }
+        continue;
       }
+      if (ip > 0) __syncthreads();  // every wave is done with the previous pass's LDS ring
+    }
+    bf16x8 kf[KB][C::KS], vf[KB][C::KS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int kr = kh + WK * w + 32 * kb + l32;
+      const bool ok = kr < nk;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        kf[kb][s] = ok ? *(const bf16x8*)(K + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
+        if (DO_DK) vf[kb][s] = ok ? *(const bf16x8*)(V + base + (size_t)kr * rs + 16 * s + 8 * half) : zero_bf16x8();
+      }
+    }
+    f32x16 dkacc[KB][C::NB], dvacc[KB][C::NB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[kb][db][r] = dvacc[kb][db][r] = 0.0f;
+
+    if (nqt > 0) {
+      const uint32_t row_bytes = (uint32_t)(rs * 2);
+      const __bf16* Qb = Q + base_q;
+      const __bf16* dOb = dO + base_q;
+      const float2* Sb = SM ? stats + sl.row0_q(z) * H + h : nullptr;
+      auto fetch = [&](__bf16* sq, __bf16* sg, float2* ss, int tile) {
+        const int r0 = tile * C::BQ_KV;
+        const size_t off = (size_t)(r0 < nq ? r0 : 0) * rs;  // no row is read past n_q
+        dma_tile<D, 64, 256>(sq, Qb + off, row_bytes, nq - r0, tid);
+        dma_tile<D, 64, 256>(sg, dOb + off, row_bytes, nq - r0, tid);
+        if constexpr (SM) dma_stats64(ss, Sb + (size_t)(r0 < nq ? r0 : 0) * H, (uint32_t)(H * 8), nq - r0, tid);
+      };
+      f32x16 sX[KB], pX[KB], sY[KB], pY[KB];
+      bf16x8 ptX[KB][2], ptY[KB][2], dsX[KB][2], dsY[KB][2];
+      // Query tile u: its slot (q_cur, g_cur), tile u-1's slot (q_prev, g_prev)
+      // and the slot that receives tile u+1 (it held tile u-2).
+      // The V stage of each step turns the previous A stage's block into P (and
+      // dS). The A stage reads the row statistics of its own tile (s_cur).
+      auto iteration = [&](__bf16* q_cur, __bf16* g_cur, float2* s_cur, __bf16* q_prev, __bf16* g_prev,
+                           __bf16* q_next, __bf16* g_next, float2* s_next, int u, int n_tiles) {
+        dma_wait();
+        __syncthreads();
+        if (u + 1 < n_tiles) fetch(q_next, g_next, s_next, u + 1);
+        kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX,
+                                                ptY, dsY, sY, pY, kf, vf, c1, c0, s_cur, l32, half, lane);
+        kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
+                                                ptX, dsX, sX, pX, kf, vf, c1, c0, s_cur, l32, half, lane);
+      };
+      // Tile 0 into slot 0, then tile 1 into slot 1 (q1, g1, s1: its DMA
+      // destinations) behind the first A stages.
+      auto prologue = [&](__bf16* q0, __bf16* g0, float2* s0, __bf16* q1, __bf16* g1, float2* s1, int n_tiles) {
+        fetch(q0, g0, s0, 0);
+        dma_wait();
+        __syncthreads();
+        if (n_tiles > 1) fetch(q1, g1, s1, 1);  // no DMA may be left in flight when the kernel ends
+        kv_step<D, MODE, ACT, true, false, false>(q0, g0, 0, q0, g0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
+                                                  pY, kf, vf, c1, c0, s0, l32, half, lane);
+        kv_step<D, MODE, ACT, true, false, true>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
+                                                 pX, kf, vf, c1, c0, s0, l32, half, lane);
+      };
+      auto epilogue = [&](__bf16* q_last, __bf16* g_last, float2* s_last) {
+        kv_step<D, MODE, ACT, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
+                                                 dsX, ptY, dsY, sY, pY, kf, vf, c1, c0, s_last, l32, half, lane);
+        kv_step<D, MODE, ACT, false, true, false>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY,
+                                                  dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, s_last, l32, half, lane);
+      };
+      if constexpr (kUnrolledRing<D, MODE>) {
+        // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
+        // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
+        // exactly nothing to dV or dK.
+        const int nqt3 = 1 + (nqt + 1) / 3 * 3;
+        prologue(sQ0, sG0, sS0, sQ1, sG1, sS1, nqt3);
+        for (int u = 1; u < nqt3; u += 3) {
+          iteration(sQ1, sG1, sS1, sQ0, sG0, sQ2, sG2, sS2, u, nqt3);
+          iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt3);
+          iteration(sQ0, sG0, sS0, sQ2, sG2, sQ1, sG1, sS1, u + 2, nqt3);
+        }
+        epilogue(sQ0, sG0, sS0);  // tile nqt3 - 1 sits in slot 0
+      } else {
+        // The three slots are parts of one array, indexed at run time. Every
+        // read names that array, so the compiler can match it against DMAs.
+        // The DMA destinations are passed through lds_opaque: the compiler does
+        // not match the reads against them and inserts no wait for the DMA in
+        // flight. The DMA of a tile is waited for explicitly (dma_wait and the
+        // barrier at the top of the next iteration) before any read of it.
+        auto q_at = [&](int i) { return sRing + (2 * i) * C::TILE; };
+        auto g_at = [&](int i) { return sRing + (2 * i + 1) * C::TILE; };
+        auto s_at = [&](int i) { return SM ? sSRing + 64 * i : sSRing; };
+        prologue(q_at(0), g_at(0), s_at(0), lds_opaque(q_at(1)), lds_opaque(g_at(1)), lds_opaque(s_at(1)), nqt);
+        int cur = 0;
+        for (int u = 1; u < nqt; ++u) {
+          const int prev = cur;
+          cur = (cur == 2) ? 0 : cur + 1;
+          const int next = (cur == 2) ? 0 : cur + 1;
+          iteration(q_at(cur), g_at(cur), s_at(cur), q_at(prev), g_at(prev), lds_opaque(q_at(next)),
+                    lds_opaque(g_at(next)), lds_opaque(s_at(next)), u, nqt);
+        }
+        epilogue(q_at(cur), g_at(cur), s_at(cur));
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int db = 0; db < C::NB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = kh + WK * w + 32 * kb + acc_row(r, half);
+          if (row < rows) {
+            const bool ok = row < nk;
+            if (DO_DK) dKb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? alpha * dkacc[kb][db][r] : 0.0f);
+            if (DO_DV) dVb[(size_t)row * rs + db * 32 + l32] = (__bf16)(ok ? dvacc[kb][db][r] : 0.0f);
+          }
+        }
+  }
   if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = nqt;
 }
 
