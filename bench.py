@@ -4,10 +4,10 @@
 
 Definitions:
 * A step is one pass of the whole hot path over one batch of resident
-  synthetic input: sigattn_fwd, then the backward (sigattn_bwd_dkdv at
-  D = 64; sigattn_bwd_dk and sigattn_bwd_dv at D = 128; then sigattn_bwd_dq),
-  one kernel per call, all on torch's current stream. This is exactly the
-  work of sigattn_fwd + sigattn_bwd.
+  synthetic input: sigattn_fwd, then the backward (sigattn_bwd_dkdv, one
+  fused dK/dV kernel, then sigattn_bwd_dq), one kernel per call, all on
+  torch's current stream. This is exactly the work of sigattn_fwd +
+  sigattn_bwd.
 * `value` is whole-step throughput in TFLOP/s. FLOPs are counted the pages'
   way (valid tokens only; backward = 2.5x forward) and divided by host wall
   time over exactly K steps, with a device synchronisation on both sides.
@@ -23,7 +23,7 @@ Definitions:
   its TFLOP/s against the FP8 dense peak and against the bf16 forward.
 * `softmax`: padding-aware softmax attention fwd+bwd on the main workload,
   with the same FLOP count, timed per call (forward: one kernel; backward:
-  row statistics, dK, dV, dQ) with HIP events on the launch stream.
+  row statistics, fused dK/dV, dQ) with HIP events on the launch stream.
 
 One GPU only. --gpus above 1 exits with a message.
 """
@@ -82,17 +82,12 @@ def run_gpu(name, steps, warmup, seed=0):
     stream = torch.cuda.current_stream(dev)
 
     # The kernels of one step, in launch order, with each kernel's algorithmic
-    # contraction FLOPs per valid score pair: fwd 4D (QK^T, PV); dQ 6D (S, dP,
-    # dQ); dK/dV 8D (S, dP, dV, dK) when fused (D = 64), else dK 6D (S, dP, dK)
-    # and dV 4D (S, dV) as two launches (D = 128).
+    # contraction FLOPs per valid score pair: fwd 4D (QK^T, PV); dK/dV 8D (S,
+    # dP, dV, dK, fused); dQ 6D (S, dP, dQ).
     a, b = w.alpha, w.bias
-    launches = [("fwd", 4, lambda: sa.sigattn_fwd(q, k, v, nq, nk, a, b, out=o))]
-    if w.D == 64:
-        launches.append(("dkdv", 8, lambda: sa.sigattn_bwd_dkdv(q, k, v, do, nq, nk, a, b, dk=dk, dv=dv)))
-    else:
-        launches.append(("dk", 6, lambda: sa.sigattn_bwd_dk(q, k, v, do, nq, nk, a, b, dk=dk)))
-        launches.append(("dv", 4, lambda: sa.sigattn_bwd_dv(q, k, do, nq, nk, a, b, dv=dv)))
-    launches.append(("dq", 6, lambda: sa.sigattn_bwd_dq(q, k, v, do, nq, nk, a, b, dq=dq)))
+    launches = [("fwd", 4, lambda: sa.sigattn_fwd(q, k, v, nq, nk, a, b, out=o)),
+                ("dkdv", 8, lambda: sa.sigattn_bwd_dkdv(q, k, v, do, nq, nk, a, b, dk=dk, dv=dv)),
+                ("dq", 6, lambda: sa.sigattn_bwd_dq(q, k, v, do, nq, nk, a, b, dq=dq))]
     nl = len(launches)
 
     def step(ev=None):

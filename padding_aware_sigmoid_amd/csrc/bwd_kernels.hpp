@@ -352,11 +352,13 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
       }
     });
     constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
-    // A hard fence every second step keeps the LDS reads two steps ahead of
-    // their MFMAs (the dV kernel, and the fused form with one key block). In
-    // the other kernels that compute dK it makes the compiler spill or fail,
+    // A hard fence every step (the fused form with one key block) or every
+    // second step (the dV kernel) keeps the LDS reads two steps ahead of
+    // their MFMAs. Measured on the fused form at D = 128: fences every 1, 2, 4
+    // steps and none, 4.05, 4.08, 4.44, 4.49 ms (L = 16K, H = 16). In the
+    // other kernels that compute dK a fence makes the compiler spill or fail,
     // so they schedule each kv_step as one region.
-    constexpr int FENCE = (MODE == KV_DV || KB == 1) ? 2 : kNoFence;
+    constexpr int FENCE = KB == 1 ? 1 : (MODE == KV_DV ? 2 : kNoFence);
     sched_step<j, nds, KB, (e1 - e0) * (DK ? 7 : 5), FENCE>();
   });
 }
