@@ -131,8 +131,8 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
 
 /*
  * The two halves of sigattn_bwd, for callers that want to place or time them
- * separately (for example, on two streams). sigattn_bwd_dq launches one kernel;
- * sigattn_bwd_dkdv launches one at D = 64 and two (dk, then dv) at D = 128.
+ * separately (for example, on two streams). Each launches one kernel;
+ * sigattn_bwd_dkdv's computes dk and dv together from one recomputed P.
  * sigattn_bwd_dkdv writes dk and dv. sigattn_bwd_dq writes dq. Arguments are as
  * for sigattn_bwd. Together they compute exactly what sigattn_bwd computes,
  * bit for bit.
@@ -151,8 +151,8 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
  * sigattn_bwd_dkdv (rainbus.top summary, 方法步骤详情 step 5: dV = P^T dO and
  * dK = alpha dS^T Q are separate contractions over the recomputed P). dv needs
  * no v. Both write tile_counts_dkdv as sigattn_bwd_dkdv does, and their outputs
- * equal its dk and dv bit for bit. At D = 128, sigattn_bwd_dkdv is these two
- * launches in sequence.
+ * equal its dk and dv bit for bit. Together they cost more than
+ * sigattn_bwd_dkdv: each recomputes the scores (and dk also dO V^T).
  */
 int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout, void* dk,
                    const int32_t* seqlens_q, const int32_t* seqlens_k,

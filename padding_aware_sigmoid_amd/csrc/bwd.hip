@@ -163,14 +163,7 @@ hipError_t launch_dkdv_bf16(int act, int mode, const void* q, const void* k, con
     constexpr int A = decltype(act_c)::value;
     if (mode == KV_DK) return only_dk(act_c);
     if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV, A>);
-    // The fused form: sigmoid at D = 64, and both activations at D = 128
-    // (one key block per wave there).
-    if constexpr (D == 128 || A == ACT_SIGMOID) return go(dkdv_bf16_kernel<D, KV_BOTH, A>);
-    // Softmax at D = 64: its row statistics push the fused form past a wave's
-    // registers. Both launches see the same lengths, so both write the same
-    // counters.
-    hipError_t e = only_dk(act_c);
-    return e != hipSuccess ? e : go(dkdv_bf16_kernel<D, KV_DV, A>);
+    return go(dkdv_bf16_kernel<D, KV_BOTH, A>);
   };
   return act == ACT_SOFTMAX ? run(std::integral_constant<int, ACT_SOFTMAX>{})
                             : run(std::integral_constant<int, ACT_SIGMOID>{});

@@ -226,8 +226,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
-// Wave w owns KB 32-row key blocks (KB = 2, 64 keys, except the fused form at
-// D = 128: KB = 1). It holds K and V as B operands, for:
+// Wave w owns KB 32-row key blocks (KB = 2, 64 keys, in the separate dK and dV
+// kernels; KB = 1 in the fused form). It holds K and V as B operands, for:
 //   S  = Q K^T   (A = Q from LDS)
 //   dP = dO V^T  (A = dO from LDS)
 // P^T and dS^T come straight from those accumulators as A operands, for:
@@ -244,15 +244,17 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__
 //   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
 //   KV_DK (S, dP, dK: 6*D) and KV_DV (S, dV: 4*D) split the work over two
 //   launches.
-// At D = 128 the K and V operands plus both accumulators for 64 keys do not
-// fit one wave's registers, so the fused form there gives each wave 32 keys
-// (KB = 1) and runs the workgroup's 256 keys as two halves of 128, each
-// streaming all query tiles. The split forms keep KB = 2.
+// The fused form gives each wave 32 keys (KB = 1) and runs the workgroup's 256
+// keys as two passes of 128, each streaming all query tiles. At D = 128 the K
+// and V operands plus both accumulators for 64 keys do not fit one wave's
+// registers; at D = 64 they do, but at the register limit, where no
+// scheduling fence fits, and the one-block form measured 13-14% faster
+// (cellbatch8k and stress8k). The split forms keep KB = 2.
 enum KvMode { KV_BOTH = 0, KV_DK = 1, KV_DV = 2 };
 
 // Key blocks of 32 rows per wave.
 template <int D, int MODE>
-constexpr int kKB = (D == 128 && MODE == KV_BOTH) ? 1 : 2;
+constexpr int kKB = MODE == KV_BOTH ? 1 : 2;
 
 // stA (softmax only): the row statistics {LSE / alpha, D} of the tile whose
 // query block qba the A stage processes. The A stage starts its accumulators
@@ -352,12 +354,12 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
       }
     });
     constexpr int nds = (j + 2 < NSTEP) ? (kind(j + 2) <= 1 ? 1 : 2) : 0;
-    // A hard fence every step (the fused form with one key block) or every
-    // second step (the dV kernel) keeps the LDS reads two steps ahead of
-    // their MFMAs. Measured on the fused form at D = 128: fences every 1, 2, 4
-    // steps and none, 4.05, 4.08, 4.44, 4.49 ms (L = 16K, H = 16). In the
-    // other kernels that compute dK a fence makes the compiler spill or fail,
-    // so they schedule each kv_step as one region.
+    // A hard fence every step (the fused form) or every second step (the dV
+    // kernel) keeps the LDS reads two steps ahead of their MFMAs. Measured on
+    // the fused form at D = 128: fences every 1, 2, 4 steps and none, 4.05,
+    // 4.08, 4.44, 4.49 ms (L = 16K, H = 16). In the separate dK kernel a fence
+    // makes the compiler spill or fail, so it schedules each kv_step as one
+    // region.
     constexpr int FENCE = KB == 1 ? 1 : (MODE == KV_DV ? 2 : kNoFence);
     sched_step<j, nds, KB, (e1 - e0) * (DK ? 7 : 5), FENCE>();
   });
@@ -365,13 +367,13 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
 
 // Whether the dK/dV query loop is unrolled over the three ring slots. Unrolled,
 // every LDS access names its slot at compile time, and the compiler does not
-// wait for the DMA into one slot before reading the others. The two kernels
-// already at the register limit (fused dK+dV at D = 64, dK at D = 128) spill
-// heavily when unrolled. They keep a runtime slot index into one array, with
-// the DMA destinations hidden from the compiler (lds_opaque), which then
-// does not wait for a DMA before their next LDS read either.
+// wait for the DMA into one slot before reading the others. The separate dK
+// kernel at D = 128 is at the register limit and spills heavily when
+// unrolled. It keeps a runtime slot index into one array, with the DMA
+// destinations hidden from the compiler (lds_opaque), which then does not
+// wait for a DMA before its next LDS read either.
 template <int D, int MODE>
-constexpr bool kUnrolledRing = !((MODE == KV_BOTH && D == 64) || (MODE == KV_DK && D == 128));
+constexpr bool kUnrolledRing = !(MODE == KV_DK && D == 128);
 
 // One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV), for the
 // attention ACT selects. With softmax each query tile's row statistics
