@@ -378,7 +378,7 @@ constexpr bool kUnrolledRing = !(MODE == KV_DK && D == 128);
 // One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV), for the
 // attention ACT selects. With softmax each query tile's row statistics
 // {LSE / alpha, D} (64 float2) ride the LDS ring beside its Q and dO.
-template <int D, int MODE, int ACT>
+template <int D, int MODE, int ACT, bool SWAP = false>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         __bf16* __restrict__ dK, __bf16* __restrict__ dV,
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   using C = BwdCfg<D>;
   constexpr bool DO_DK = MODE != KV_DV, DO_DV = MODE != KV_DK;
   constexpr bool SM = ACT == ACT_SOFTMAX;
-  constexpr bool UR = kUnrolledRing<D, MODE>;
+  constexpr bool UR = SWAP || kUnrolledRing<D, MODE>;
   constexpr int TS = UR ? C::TILE : 8;  // the runtime-indexed ring lives in sRing instead
   __shared__ __attribute__((aligned(1024))) __bf16 sQ0[TS];
   __shared__ __attribute__((aligned(1024))) __bf16 sQ1[TS];
@@ -405,14 +405,19 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
   const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;
   const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, sl, rank_lds);
   const int z = tcd.z, h = tcd.h, t = tcd.m;
-  const int nq = sl.nq(z);
-  const int nk = sl.nk(z);
-  const float c0 = sl.c0_for(c0_base, nk);
+  // With SWAP the roles of queries and keys are exchanged (the sigmoid dQ
+  // kernel at D = 64): "keys" here are the query rows the workgroup owns,
+  // "queries" the key rows it streams, K and V arrive as Q and dO, dO and Q
+  // as V and K, and the dK written is dQ. The per-sample bias still follows
+  // the true key count.
+  const int nq = SWAP ? sl.nk(z) : sl.nq(z);
+  const int nk = SWAP ? sl.nq(z) : sl.nk(z);
+  const float c0 = sl.c0_for(c0_base, sl.nk(z));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)H * D;
-  const size_t base = (sl.row0_k(z) * H + h) * D;    // K, V, dK and dV
-  const size_t base_q = (sl.row0_q(z) * H + h) * D;  // Q and dO
-  const int rows = sl.rows(nk);                       // rows of this sample in dK, dV
+  const size_t base = ((SWAP ? sl.row0_q(z) : sl.row0_k(z)) * H + h) * D;    // K, V, dK and dV
+  const size_t base_q = ((SWAP ? sl.row0_k(z) : sl.row0_q(z)) * H + h) * D;  // Q and dO
+  const int rows = sl.rows(nk);                                              // rows of this sample in dK, dV
   const int k0 = t * C::BK_KV;
   __bf16* dKb = dK + base;
   __bf16* dVb = dV + base;
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
     return;
   }
 
-  constexpr int KB = kKB<D, MODE>;
+  constexpr int KB = SWAP ? 1 : kKB<D, MODE>;
   constexpr int WK = 32 * KB;           // keys per wave
   constexpr int SUB = C::NWAVE * WK;    // keys per pass over the queries
   const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
@@ -493,9 +498,9 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
         dma_wait();
         __syncthreads();
         if (u + 1 < n_tiles) fetch(q_next, g_next, s_next, u + 1);
-        kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX,
+        kv_step<D, MODE, ACT, true, true, true, KB>(q_cur, g_cur, 0, q_prev, g_prev, 0, sX, pX, dkacc, dvacc, ptX, dsX,
                                                 ptY, dsY, sY, pY, kf, vf, c1, c0, s_cur, l32, half, lane);
-        kv_step<D, MODE, ACT, true, true, true>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
+        kv_step<D, MODE, ACT, true, true, true, KB>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
                                                 ptX, dsX, sX, pX, kf, vf, c1, c0, s_cur, l32, half, lane);
       };
       // Tile 0 into slot 0, then tile 1 into slot 1 (q1, g1, s1: its DMA
@@ -505,18 +510,18 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict
         dma_wait();
         __syncthreads();
         if (n_tiles > 1) fetch(q1, g1, s1, 1);  // no DMA may be left in flight when the kernel ends
-        kv_step<D, MODE, ACT, true, false, false>(q0, g0, 0, q0, g0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
+        kv_step<D, MODE, ACT, true, false, false, KB>(q0, g0, 0, q0, g0, 0, sX, pX, dkacc, dvacc, ptX, dsX, ptY, dsY, sY,
                                                   pY, kf, vf, c1, c0, s0, l32, half, lane);
-        kv_step<D, MODE, ACT, true, false, true>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
+        kv_step<D, MODE, ACT, true, false, true, KB>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
                                                  pX, kf, vf, c1, c0, s0, l32, half, lane);
       };
       auto epilogue = [&](__bf16* q_last, __bf16* g_last, float2* s_last) {
-        kv_step<D, MODE, ACT, false, true, true>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
+        kv_step<D, MODE, ACT, false, true, true, KB>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
                                                  dsX, ptY, dsY, sY, pY, kf, vf, c1, c0, s_last, l32, half, lane);
-        kv_step<D, MODE, ACT, false, true, false>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY,
+        kv_step<D, MODE, ACT, false, true, false, KB>(q_last, g_last, 0, q_last, g_last, 1, sY, pY, dkacc, dvacc, ptY,
                                                   dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, s_last, l32, half, lane);
       };
-      if constexpr (kUnrolledRing<D, MODE>) {
+      if constexpr (UR) {
         // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
         // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
         // exactly nothing to dV or dK.

@@ -43,12 +43,14 @@ def short_name(kernel: str) -> str | None:
     """The bench name of a sigattn kernel from its demangled or mangled name,
     else None. Sigmoid bf16: fwd, dq, dk, dv, dkdv; softmax: the same with an
     sm_ prefix, plus sm_rowstats; fp32 kernels carry a _fp32 suffix; the FP8
-    path's kernels are fp8_fwd and fp8_quantize."""
+    path's kernels are fp8_fwd and fp8_quantize. The dK/dV kernel with queries
+    and keys exchanged (its last template argument true) computes dQ."""
     m = re.search(r"sigattn::(\w+?)_kernel<([^>]*)>", kernel)
     if m is not None:
         base, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
         ints = [int(a) for a in args if a.isdigit()]
         float_arg = "float" in args
+        swapped = "true" in args
     else:  # e.g. _ZN7sigattn16dkdv_bf16_kernelILi128ELi1ELi0EEEv...
         m = re.search(r"_ZN7sigattn\d+(\w+?)_kernelI(.*?)EEv", kernel)
         if m is None:
@@ -56,6 +58,7 @@ def short_name(kernel: str) -> str | None:
         base = m.group(1)
         ints = [int(x) for x in re.findall(r"Li(\d+)E", m.group(2))]
         float_arg = m.group(2).startswith("f")
+        swapped = "Lb1E" in m.group(2)
     sm = base.startswith("sm_")
     core = base[3:] if sm else base
     if core == "rowstats":
@@ -69,7 +72,7 @@ def short_name(kernel: str) -> str | None:
     if dtype == "bf16" and kind == "dq" and len(ints) > 1:
         sm = sm or ints[1] == 1
     if dtype == "bf16" and kind == "dkdv" and len(ints) > 1:
-        kind = {0: "dkdv", 1: "dk", 2: "dv"}[ints[1]]
+        kind = "dq" if swapped else {0: "dkdv", 1: "dk", 2: "dv"}[ints[1]]
         sm = sm or (len(ints) > 2 and ints[2] == 1)
     return ("sm_" if sm else "") + kind + ("" if dtype == "bf16" else "_fp32")
 

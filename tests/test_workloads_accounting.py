@@ -77,6 +77,9 @@ def test_profile_kernel_names():
         "void sigattn::dkdv_bf16_kernel<128, 1, 0>(...)": "dk",
         "void sigattn::dkdv_bf16_kernel<128, 2, 1>(...)": "sm_dv",
         "void sigattn::dkdv_bf16_kernel<64, 0, 0>(...)": "dkdv",
+        "void sigattn::dkdv_bf16_kernel<64, 1, 0, true>(...)": "dq",
+        "_ZN7sigattn16dkdv_bf16_kernelILi64ELi1ELi0ELb1EEEvPKDF16b": "dq",
+        "_ZN7sigattn16dkdv_bf16_kernelILi64ELi1ELi0ELb0EEEvPKDF16b": "dk",
         "void sigattn::dq_bf16_kernel<128, 1>(...)": "sm_dq",
         "void sigattn::dq_bf16_kernel<64, 0>(...)": "dq",
         "void sigattn::sm_fwd_bf16_kernel<128>(...)": "sm_fwd",
