@@ -60,6 +60,10 @@ CASES = [
     ("nq!=nk", 2, 260, 1, 128, [260, 65], [129, 260]),
     ("edge-lengths", 4, 192, 1, 64, [0, 1, 128, 64], [192, 1, 0, 65]),
     ("single-tile", 1, 64, 3, 128, [40], [64]),
+    # both sides of the fused dK/dV kernel's 128-row passes (a second pass
+    # wholly in padding: n = 1, 127, 128) and of its 256-row workgroup tiles
+    ("passes-d128", 6, 400, 1, 128, [385, 256, 129, 128, 127, 1], [1, 127, 128, 129, 256, 385]),
+    ("passes-d64", 6, 400, 1, 64, [385, 256, 129, 128, 127, 1], [1, 127, 128, 129, 256, 385]),
 ]
 
 

@@ -40,6 +40,9 @@ CASES = [
     ("bf16-d128-nokeys", "bf16", 2, 260, 1, 128, [260, 90], [0, 260]),
     ("fp32-d64", "fp32", 2, 200, 2, 64, [200, 77], [150, 200]),
     ("fp32-d128", "fp32", 2, 130, 1, 128, [65, 130], [130, 1]),
+    # both sides of the fused dK/dV kernel's 128-row passes and 256-row tiles
+    ("bf16-d128-passes", "bf16", 6, 400, 1, 128, [1, 127, 128, 129, 256, 385], [385, 256, 129, 128, 127, 1]),
+    ("bf16-d64-passes", "bf16", 6, 400, 1, 64, [1, 127, 128, 129, 256, 385], [385, 256, 129, 128, 127, 1]),
 ]
 
 

@@ -37,6 +37,10 @@ CASES = [
     ("bf16-d128", "bf16", 3, 333, 2, 128, [333, 0, 200], [100, 5, 333]),
     ("fp32-d64", "fp32", 2, 200, 2, 64, [200, 77], [150, 200]),
     ("fp32-d128", "fp32", 2, 130, 1, 128, [65, 130], [130, 1]),
+    # lengths on both sides of the fused dK/dV kernel's 128-row passes and
+    # 256-row workgroup tiles (a second pass wholly in padding: 1, 127, 128)
+    ("bf16-d128-passes", "bf16", 6, 400, 1, 128, [1, 127, 128, 129, 256, 385], [385, 256, 129, 128, 127, 1]),
+    ("bf16-d64-passes", "bf16", 6, 400, 1, 64, [1, 127, 128, 129, 256, 385], [385, 256, 129, 128, 127, 1]),
 ]
 
 
