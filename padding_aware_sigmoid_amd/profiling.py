@@ -28,7 +28,7 @@ ROOT = pathlib.Path(__file__).resolve().parent.parent
 KERNEL_SOURCES = ["padding_aware_sigmoid_amd/csrc/common.hpp", "padding_aware_sigmoid_amd/csrc/fwd.hip",
                   "padding_aware_sigmoid_amd/csrc/bwd_kernels.hpp", "padding_aware_sigmoid_amd/csrc/bwd.hip",
                   "padding_aware_sigmoid_amd/csrc/bwd_softmax_dk128.hip", "padding_aware_sigmoid_amd/csrc/softmax.hip",
-                  "padding_aware_sigmoid_amd/csrc/fp8.hip"]
+                  "padding_aware_sigmoid_amd/csrc/fp8.hip", "padding_aware_sigmoid_amd/build.py"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
