@@ -58,7 +58,7 @@ enum Act { ACT_SIGMOID = 0, ACT_SOFTMAX = 1 };
 // the in-flight DMA apart from the reads of the other two slots and does not
 // wait for it before them.
 template <int D, int ACT>
-__global__ __launch_bounds__(256) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                       __bf16* __restrict__ dQ, const float2* __restrict__ stats,
                                                       SeqLayout sl, int Z, int H, float alpha, float c1,
@@ -408,7 +408,7 @@ constexpr bool kUnrolledRing = !(MODE == KV_DK && D == 128);
 // attention ACT selects. With softmax each query tile's row statistics
 // {LSE / alpha, D} (64 float2) ride the LDS ring beside its Q and dO.
 template <int D, int MODE, int ACT, bool SWAP = false>
-__global__ __launch_bounds__(256) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                                         __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                         const float2* __restrict__ stats, SeqLayout sl, int Z, int H,

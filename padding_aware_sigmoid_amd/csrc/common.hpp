@@ -103,6 +103,16 @@ __device__ __forceinline__ T* ring(T* a, T* b, T* c) {
   else return c;
 }
 
+// Waves per SIMD a bf16 attention kernel is built for (the second argument of
+// __launch_bounds__: the compiler keeps each wave within 512 / that many
+// registers). At D = 64 the forward, the fused dK/dV and dQ fit 256 registers
+// with a few spills and 49 KB of LDS, so two workgroups share a CU and each
+// SIMD interleaves two waves: measured 10-21% faster per kernel on
+// cellbatch8k and stress8k than one wave per SIMD without spills. At D = 128
+// they need 430-480 registers and 97 KB of LDS: one wave per SIMD.
+template <int D>
+constexpr int kWavesPerSimd = D == 64 ? 2 : 1;
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = BEGIN .. END-1.
 // The index is a constant expression inside f, which the scheduling builtins
 // need.

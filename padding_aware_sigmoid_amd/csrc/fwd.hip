@@ -187,7 +187,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, con
 // the barrier cannot touch the slot the DMA is filling and does not wait for
 // the DMA before them.
 template <int D>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                        SeqLayout sl, int Z, int H, float c1, float c0_base,
                                                        int32_t* __restrict__ tile_counts) {

@@ -216,7 +216,7 @@ __device__ __forceinline__ void sm_accumulate_pv(f32x16 (&oT)[2][SmCfg<D>::NB], 
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void sm_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                           float* __restrict__ LSE, SeqLayout sl, int Z, int H,
                                                           float c1) {
