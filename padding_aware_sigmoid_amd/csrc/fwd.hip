@@ -54,14 +54,6 @@ __device__ __forceinline__ void scores_t(f32x16 (&sacc)[2], const __bf16* sK, in
   }
 }
 
-// P = sigma(S) in registers, packed as the A operands (two k-steps of 16 keys) of P V.
-__device__ __forceinline__ void sigma_pack(bf16x8 (&p)[2][2], const f32x16 (&sacc)[2], float c1, float c0) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(sacc[qb][r], c1, c0);
-}
-
 // O += P V for one 32-key block kb of a V tile.
 template <int D>
 __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], const bf16x8 (&p)[2][2],
