@@ -75,6 +75,18 @@ def test_bf16_parity(case):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_many_samples(D):
+    """More samples than the tile scheduler ranks (256): the unranked mapping,
+    with lengths 0..L and Z * H not a multiple of 8."""
+    Z, L, H = 301, 40, 1
+    rng = np.random.default_rng(D)
+    nq = rng.integers(0, L + 1, Z)
+    nk = rng.integers(0, L + 1, Z)
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=77)
+    _check_full(q, k, v, do, nq, nk, 1 / math.sqrt(D), -math.log(L), BF16_TOL, f"many-samples-D{D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_fp32_validation_build(D):
     """The tiny workload (Z=2, H=2, L=256, lengths [256, 160]) in fp32, at 1e-5."""
     w = workloads.WORKLOADS["tiny"]
