@@ -51,6 +51,8 @@ enum Act { ACT_SIGMOID = 0, ACT_SOFTMAX = 1 };
 // dQ += dS K. That product takes K from LDS through transposed reads.
 // Key tiles of 64 rows stream through a 3-slot LDS ring by DMA. Per 32-key
 // block, the previous block's dQ MFMAs run beside this block's sigma and dS.
+// At D = 128 each tile runs as one explicit stream of steps that reads every
+// LDS operand two steps ahead.
 // Tile t-2 is last read in iteration t-1 (the dQ of its second block), so the
 // DMA of tile t+1 into its slot starts only after iteration t's barrier.
 // Each slot is its own LDS variable and the key loop is unrolled by three, so
@@ -150,8 +152,97 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
     bf16x8 ds_prev[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) ds_prev[qb][0] = ds_prev[qb][1] = zero_bf16x8();
-    // One key tile in slot S; slot P holds the tile before it, slot N receives the next.
-    auto iteration = [&](auto s_c, auto p_c, auto n_c, int t) {
+    // One key tile in slot S; slot P holds the tile before it, slot N receives
+    // the next. The tile's two 32-key blocks run as one stream of steps, each
+    // one LDS read and two MFMAs (one per query block):
+    //   block steps 0 .. KS - 1: S^T of this block (K read by rows);
+    //   block steps KS .. 2 KS - 1: dP^T of this block (V read by rows), beside
+    //     P = sigma(S), written over the scores;
+    //   block steps 2 KS .. 2 KS + 2 NB - 1: dQ += dS K of the previous block
+    //     (K read transposed), beside dS of this block.
+    // Each step's operand is read two steps ahead, across the block boundary.
+    // Splitting sigma from dS this way spreads the VALU work over two thirds of
+    // the steps instead of one third: 1% faster than all of it beside dQ.
+    constexpr int NA = 2 * C::KS, NSB = NA + 2 * C::NB, NT = 2 * NSB;
+    constexpr int NE = 32;  // scores per lane and block: two query blocks of 16
+    auto iteration_stream = [&](auto s_c, auto p_c, auto n_c, int t) {
+      constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
+      const __bf16* const sk = ring<S>(sK0, sK1, sK2);
+      const __bf16* const sv = ring<S>(sV0, sV1, sV2);
+      const __bf16* const skp = ring<P>(sK0, sK1, sK2);
+      dma_wait();
+      __syncthreads();  // tile t is in LDS, and every wave is done with iteration t-1
+      if (t + 1 < nkt3) fetch(ring<N>(sK0, sK1, sK2), ring<N>(sV0, sV1, sV2), t + 1);  // slot N held tile t-2
+      auto read = [&](auto gc) -> bf16x8 {
+        constexpr int g = decltype(gc)::value, blk = g / NSB, j = g % NSB;
+        if constexpr (j < NA) {
+          return lds_nat<D>(j >= C::KS ? sv : sk, blk * 32 + l32, 2 * (j % C::KS) + half);
+        } else {
+          constexpr int i = j - NA, db = i >> 1, ks = i & 1;
+          return lds_tr<D>(blk == 0 ? skp : sk, (1 - blk) * 32 + ks * 16, db * 32, lane);
+        }
+      };
+      f32x16 sacc[2], pacc[2];
+      bf16x8 ds_mid[2][2];  // dS of block 0, for block 1's dQ
+      bf16x8 ops[3];
+      ops[0] = read(std::integral_constant<int, 0>{});
+      ops[1] = read(std::integral_constant<int, 1>{});
+      static_for<0, NT>([&](auto gc) {
+        constexpr int g = decltype(gc)::value, blk = g / NSB, j = g % NSB;
+        if constexpr (g + 2 < NT) ops[(g + 2) % 3] = read(std::integral_constant<int, g + 2>{});
+        const bf16x8 op = ops[g % 3];
+        if constexpr (j == 0) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
+        }
+        if constexpr (j < NA) {
+          constexpr int s = j % C::KS;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            if constexpr (j >= C::KS)
+              pacc[qb] = mfma32(op, dof[qb][s], pacc[qb]);
+            else
+              sacc[qb] = mfma32(op, qf[qb][s], sacc[qb]);
+          }
+        } else {
+          constexpr int i = j - NA, db = i >> 1, ks = i & 1;
+          const bf16x8 (&dsB)[2][2] = blk == 0 ? ds_prev : ds_mid;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) acc[qb][db] = mfma32(dsB[qb][ks], op, acc[qb][db]);
+        }
+        // P = sigma(S) in place beside the dP^T MFMAs (from the second of them,
+        // once the last S^T MFMA has landed), dS beside the dQ MFMAs.
+        constexpr int NP = C::KS - 1;
+        constexpr bool PST = j > C::KS && j < NA, DST = j >= NA;
+        constexpr int p0 = PST ? (j - C::KS - 1) * NE / NP : 0, p1 = PST ? (j - C::KS) * NE / NP : 0;
+        constexpr int d0 = DST ? (j - NA) * NE / (NSB - NA) : 0, d1 = DST ? (j - NA + 1) * NE / (NSB - NA) : 0;
+        bf16x8 (&dsV)[2][2] = blk == 0 ? ds_mid : ds_prev;
+        static_for<p0, p1>([&](auto ec) {
+          constexpr int e = decltype(ec)::value, qb = e >> 4, r = e & 15;
+          if constexpr (ACT == ACT_SIGMOID)
+            sacc[qb][r] = sigmoid_dot(sacc[qb][r], c1, c0);
+          else
+            sacc[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c1, -st[qb].x));
+        });
+        static_for<d0, d1>([&](auto ec) {
+          constexpr int e = decltype(ec)::value, qb = e >> 4, r = e & 15;
+          const float p = sacc[qb][r];
+          if constexpr (ACT == ACT_SIGMOID)
+            dsV[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
+          else
+            dsV[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - st[qb].y));
+        });
+        constexpr int nds = g + 2 < NT ? ((g + 2) % NSB < NA ? 1 : 2) : 0;
+        constexpr int nvalu = (p1 - p0) * (ACT == ACT_SIGMOID ? 4 : 2) + (d1 - d0) * 3;
+        sched_step<g, nds, 2, nvalu, 1>();
+      });
+    };
+    // The same tile in plain loops (D = 64): S^T and dP^T of a block, then the
+    // previous block's dQ MFMAs beside this block's sigma and dS, scheduled by
+    // the compiler.
+    auto iteration_plain = [&](auto s_c, auto p_c, auto n_c, int t) {
       constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
       __bf16* const sk = ring<S>(sK0, sK1, sK2);
       __bf16* const sv = ring<S>(sV0, sV1, sV2);
@@ -195,6 +286,19 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
           }
         interleave_mfma_valu<4 * C::KS + 2 * C::NB * 2, 6>();
       }
+    };
+    // At D = 128 the explicit step stream keeps each LDS read four MFMAs ahead
+    // of its use; in plain loops the compiler leaves a third of the reads right
+    // before their MFMA. Measured at L = 16K, H = 16: 2.85 ms against 3.13 (a
+    // fence every step or every second step: the same). At D = 64 (softmax dQ;
+    // sigmoid takes the swapped dK/dV kernel) the stream spills 47 registers
+    // and the softmax backward ran 16% slower on cellbatch8k, so it keeps the
+    // plain loops.
+    auto iteration = [&](auto s_c, auto p_c, auto n_c, int t) {
+      if constexpr (D == 128)
+        iteration_stream(s_c, p_c, n_c, t);
+      else
+        iteration_plain(s_c, p_c, n_c, t);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
