@@ -145,11 +145,12 @@ hipError_t launch_dkdv_bf16(int act, int mode, const void* q, const void* k, con
                             void* dk, void* dv, const void* stats, SeqLayout sl, int Z, int H, float alpha, float c1,
                             float c0, int32_t* tc, hipStream_t st) {
   using C = BwdCfg<D>;
-  const long long blocks = (long long)Z * H * ((sl.L + C::BK_KV - 1) / C::BK_KV);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv, (const float2*)stats, sl, Z,
-                       H, alpha, c1, c0, tc);
+  // One workgroup per kKeysPerWg keys of each (sample, head) pair.
+  auto go = [&](auto kern, int keys_per_wg) {
+    const long long blocks = (long long)Z * H * ((sl.L + keys_per_wg - 1) / keys_per_wg);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk, (__bf16*)dv,
+                       (const float2*)stats, sl, Z, H, alpha, c1, c0, tc);
     return hipGetLastError();
   };
   auto only_dk = [&](auto act_c) -> hipError_t {
@@ -157,13 +158,13 @@ hipError_t launch_dkdv_bf16(int act, int mode, const void* q, const void* k, con
     if constexpr (D == 128 && A == ACT_SOFTMAX)
       return launch_dk_bf16_softmax_d128(q, k, v, dout, dk, stats, sl, Z, H, alpha, c1, tc, st);
     else
-      return go(dkdv_bf16_kernel<D, KV_DK, A>);
+      return go(dkdv_bf16_kernel<D, KV_DK, A>, kKeysPerWg<D, KV_DK, false>);
   };
   auto run = [&](auto act_c) -> hipError_t {
     constexpr int A = decltype(act_c)::value;
     if (mode == KV_DK) return only_dk(act_c);
-    if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV, A>);
-    return go(dkdv_bf16_kernel<D, KV_BOTH, A>);
+    if (mode == KV_DV) return go(dkdv_bf16_kernel<D, KV_DV, A>, kKeysPerWg<D, KV_DV, false>);
+    return go(dkdv_bf16_kernel<D, KV_BOTH, A>, kKeysPerWg<D, KV_BOTH, false>);
   };
   return act == ACT_SOFTMAX ? run(std::integral_constant<int, ACT_SOFTMAX>{})
                             : run(std::integral_constant<int, ACT_SIGMOID>{});
@@ -184,15 +185,17 @@ hipError_t launch_dq_bf16(int act, const void* q, const void* k, const void* v, 
   if constexpr (D == 64) {
     if (act == ACT_SIGMOID) {
       // Sigmoid dQ at D = 64 runs the dK/dV kernel with queries and keys
-      // exchanged: the workgroup owns 256 query rows in two passes of 128 (one
-      // 32-row block per wave), streams K and V, and its "dK" is dQ. dS is
+      // exchanged: a workgroup owns 128 query rows (one 32-row block per
+      // wave), streams K and V, and its "dK" is dQ. dS is
       // symmetric in the exchange (sigma of the same score, dP^T = V dO^T).
-      // At 248 registers two waves share a SIMD; 14% faster than
+      // At 240 registers two waves share a SIMD; 14% faster than
       // dq_bf16_kernel on stress8k. At D = 128 it measured 3% slower, and
       // softmax needs row statistics per owned row, which that kernel does
       // not take.
       static_assert(C::BQ_DQ == C::BK_KV, "the exchanged kernel tiles the queries as the dK/dV kernel tiles keys");
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DK, ACT_SIGMOID, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+      constexpr int R = kKeysPerWg<D, KV_DK, true>;  // query rows per workgroup
+      const long long wgs = (long long)Z * H * ((sl.L + R - 1) / R);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, KV_DK, ACT_SIGMOID, true>), dim3((unsigned)wgs), dim3(256), 0, st,
                          (const __bf16*)k, (const __bf16*)q, (const __bf16*)dout, (const __bf16*)v, (__bf16*)dq,
                          (__bf16*)nullptr, (const float2*)nullptr, sl, Z, H, alpha, c1, c0, tc);
       return hipGetLastError();

@@ -27,7 +27,7 @@ struct BwdCfg {
   static constexpr int NWAVE = 4;       // one wave per SIMD
   static constexpr int BQ_DQ = 256;     // dQ kernel: query rows per workgroup
   static constexpr int BK_DQ = 64;      // dQ kernel: keys per LDS tile
-  static constexpr int BK_KV = 256;     // dK/dV kernel: key rows per workgroup
+  static constexpr int BK_KV = 256;     // dK/dV kernel: key rows per tile_counts entry (1 or 2 workgroups)
   static constexpr int BQ_KV = 64;      // dK/dV kernel: queries per LDS tile
   static constexpr int KS = D / 16;     // MFMA k-steps over the head dim
   static constexpr int NB = D / 32;     // 32-wide column blocks of the gradients
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
 //   KV_BOTH (dK and dV together) shares S between them: 8*D MFMA FLOP per pair.
 //   KV_DK (S, dP, dK: 6*D) and KV_DV (S, dV: 4*D) split the work over two
 //   launches.
-// The fused form gives each wave 32 keys (KB = 1) and runs the workgroup's 256
-// keys as two passes of 128, each streaming all query tiles. At D = 128 the K
+// The fused form gives each wave 32 keys (KB = 1), so a workgroup covers 128
+// keys (kKeysPerWg) and streams all query tiles once for them. At D = 128 the K
 // and V operands plus both accumulators for 64 keys do not fit one wave's
 // registers; at D = 64 they do, but at the register limit, where no
 // scheduling fence fits, and the one-block form measured 13-14% faster
@@ -508,6 +508,17 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
 template <int D, int MODE>
 constexpr bool kUnrolledRing = !(MODE == KV_DK && D == 128);
 
+// Keys per workgroup: 4 waves of 32 KB keys, 128 in the one-block form
+// (KB = 1: the fused kernel and the exchanged dQ), 256 in the split kernels.
+// A tile of BK_KV keys (the unit of tile_counts) is then one or two
+// workgroups; the first of them writes its count. Workgroups of 128 keys
+// make a launch's last round shorter when sample lengths differ (a padded
+// batch finishes with its shortest samples' workgroups), and measured
+// registers below the earlier form of two passes of 128 keys per workgroup
+// (459 against 476 at D = 128).
+template <int D, int MODE, bool SWAP>
+constexpr int kKeysPerWg = BwdCfg<D>::NWAVE * 32 * (SWAP ? 1 : kKB<D, MODE>);
+
 // One launch computes what MODE selects (KV_BOTH, KV_DK or KV_DV), for the
 // attention ACT selects. With softmax each query tile's row statistics
 // {LSE / alpha, D} (64 float2) ride the LDS ring beside its Q and dO.
@@ -535,8 +546,11 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
   __shared__ __attribute__((aligned(1024))) __bf16 sRing[UR ? 8 : 6 * C::TILE];
   __shared__ __attribute__((aligned(64))) float2 sSRing[SM && !UR ? 3 * 64 : 1];
   __shared__ int rank_lds[kMaxRankedSamples];
+  constexpr int KT = kKeysPerWg<D, MODE, SWAP>;
+  constexpr int WPT = C::BK_KV / KT;  // workgroups per tile of tile_counts
   const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;
-  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_kt, sl, rank_lds);
+  const int n_wt = (sl.L + KT - 1) / KT;
+  const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_wt, sl, rank_lds);
   const int z = tcd.z, h = tcd.h, t = tcd.m;
   // With SWAP the roles of queries and keys are exchanged (the sigmoid dQ
   // kernel at D = 64): "keys" here are the query rows the workgroup owns,
@@ -551,44 +565,33 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
   const size_t base = ((SWAP ? sl.row0_q(z) : sl.row0_k(z)) * H + h) * D;    // K, V, dK and dV
   const size_t base_q = ((SWAP ? sl.row0_k(z) : sl.row0_q(z)) * H + h) * D;  // Q and dO
   const int rows = sl.rows(nk);                                              // rows of this sample in dK, dV
-  const int k0 = t * C::BK_KV;
+  const int k0 = t * KT;
   __bf16* dKb = dK + base;
   __bf16* dVb = dV + base;
 
   if (k0 >= nk) {
-    const int rows_here = min(C::BK_KV, rows - k0);
+    const int rows_here = min(KT, rows - k0);
     const bf16x8 zz = zero_bf16x8();
     for (int c = tid; c < rows_here * (D / 8); c += 256) {
       const size_t off = (size_t)(k0 + c / (D / 8)) * rs + (c % (D / 8)) * 8;
       if (DO_DK) *(bf16x8*)(dKb + off) = zz;
       if (DO_DV) *(bf16x8*)(dVb + off) = zz;
     }
-    if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = 0;
+    if (tile_counts != nullptr && tid == 0 && t % WPT == 0) tile_counts[((size_t)z * H + h) * n_kt + t / WPT] = 0;
     return;
   }
 
   constexpr int KB = SWAP ? 1 : kKB<D, MODE>;
   constexpr int WK = 32 * KB;           // keys per wave
-  constexpr int SUB = C::NWAVE * WK;    // keys per pass over the queries
+  static_assert(C::NWAVE * WK == KT, "the workgroup's waves cover its keys");
   const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
-  constexpr int NPASS = C::BK_KV / SUB;
-  // One pass over the query tiles per SUB keys (two passes when KB = 1). A
-  // second pass that lies wholly in padding only writes its zero rows.
-  for (int ip = 0; ip < NPASS; ++ip) {
-    const int kh = k0 + ip * SUB;
-    if constexpr (NPASS > 1) {
-      if (kh >= nk) {
-        const int rows_here = min(SUB, rows - kh);
-        const bf16x8 zz = zero_bf16x8();
-        for (int c = tid; c < rows_here * (D / 8); c += 256) {
-          const size_t off = (size_t)(kh + c / (D / 8)) * rs + (c % (D / 8)) * 8;
-          if (DO_DK) *(bf16x8*)(dKb + off) = zz;
-          if (DO_DV) *(bf16x8*)(dVb + off) = zz;
-        }
-        continue;
-      }
-      if (ip > 0) __syncthreads();  // every wave is done with the previous pass's LDS ring
-    }
+  // One pass over the query tiles for the workgroup's keys kh .. kh + KT - 1.
+  // The loop runs once. Written as a plain block instead, the same code
+  // compiled to 502 registers instead of 459 (fused kernel, D = 128), 56
+  // spilled registers instead of 13 (D = 64), and the exchanged dQ to 258
+  // (one wave per SIMD) instead of 240.
+  for (int pass = 0; pass < 1; ++pass) {
+    const int kh = k0;
     bf16x8 kf[KB][C::KS], vf[KB][C::KS];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -702,7 +705,7 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
           }
         }
   }
-  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_kt + t] = nqt;
+  if (tile_counts != nullptr && tid == 0 && t % WPT == 0) tile_counts[((size_t)z * H + h) * n_kt + t / WPT] = nqt;
 }
 
 // The softmax dK kernel at D = 128 lives in its own translation unit, built

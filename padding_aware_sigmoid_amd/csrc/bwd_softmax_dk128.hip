@@ -13,6 +13,7 @@ hipError_t launch_dk_bf16_softmax_d128(const void* q, const void* k, const void*
                                        int32_t* tc, hipStream_t st) {
   using C = BwdCfg<128>;
   const long long blocks = (long long)Z * H * ((sl.L + C::BK_KV - 1) / C::BK_KV);
+  static_assert(kKeysPerWg<128, KV_DK, false> == C::BK_KV, "one workgroup per key tile");
   hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DK, ACT_SOFTMAX>), dim3((unsigned)blocks), dim3(256), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (__bf16*)dk,
                      (__bf16*)nullptr, (const float2*)stats, sl, Z, H, alpha, c1, 0.0f, tc);
