@@ -113,8 +113,10 @@ def counter_means(pmc_dirs: list[pathlib.Path]) -> dict:
 # Ratios read off the SQ counters. SQ_WAVE_CYCLES, SQ_WAIT_ANY and
 # SQ_ACTIVE_INST_VALU count wave-cycles in units of 4 clocks;
 # SQ_VALU_MFMA_BUSY_CYCLES counts SIMD clocks. With one wave per SIMD (every
-# bf16 kernel here), 4 * SQ_WAVE_CYCLES is the SIMD clocks the waves were
-# resident, so the MFMA-busy fraction needs no assumption about the clock.
+# bf16 kernel at D = 128, the head size these counters are taken at),
+# 4 * SQ_WAVE_CYCLES is the SIMD clocks the waves were resident, so the
+# MFMA-busy fraction needs no assumption about the clock. At two waves per
+# SIMD (D = 64) it would read half the true fraction.
 DERIVED = (
     ("VALU instr / MFMA", ("SQ_INSTS_VALU", "SQ_INSTS_MFMA"), lambda a, b: a / b),
     ("transcendental instr / MFMA", ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"), lambda a, b: a / b),
