@@ -56,7 +56,10 @@
 extern "C" {
 #endif
 
-typedef enum { SIGATTN_BF16 = 0, SIGATTN_FP32 = 1 } sigattn_dtype;
+/* Every enum below carries a last enumerator of 0x7fffffff that names nothing:
+ * it keeps the type int-sized and every int value in its range, so an unknown
+ * value passed by a caller is rejected with a status, never undefined. */
+typedef enum { SIGATTN_BF16 = 0, SIGATTN_FP32 = 1, SIGATTN_DTYPE_INT_RANGE_ = 0x7fffffff } sigattn_dtype;
 
 typedef enum {
   SIGATTN_OK = 0,
@@ -64,7 +67,7 @@ typedef enum {
                                  pointer, non-finite alpha/bias, grid too large */
   SIGATTN_EUNSUPPORTED = -2,  /* unknown dtype */
   SIGATTN_EHIP = -3,          /* a HIP launch failed; see sigattn_last_error() */
-  SIGATTN_EWORKSPACE = -4     /* workspace smaller than sigattn_workspace_size() */
+  SIGATTN_EWORKSPACE = -4     /* workspace smaller than sigattn_softmax_bwd_workspace_size() */
 } sigattn_status;
 
 /* Where each sample's rows live (sigattn_fwd_ex, sigattn_bwd_ex).
@@ -73,22 +76,35 @@ typedef enum {
  *  PACKED: tensors are [T, H, D], the samples' valid rows back to back with no
  *          padding; seq_q and seq_k are int32[Z + 1] cumulative offsets (sample
  *          z owns rows seq[z] .. seq[z+1] - 1, so n = seq[z+1] - seq[z]). L is an
- *          upper bound on every length: rows of a longer sample past L are
- *          neither read nor written. Q, O, dO and dQ use seq_q; K, V, dK and dV
- *          use seq_k. T is implied by the offsets and never passed.
- * The varlen layout is the packed alternative to padding that the rainbus.top
- * summary ("局限与改进") and paperlayer.ai (section 3) point to for batches of
- * very unequal lengths. */
-typedef enum { SIGATTN_LAYOUT_PADDED = 0, SIGATTN_LAYOUT_PACKED = 1 } sigattn_layout;
+ *          upper bound on every length (see the contract at sigattn_fwd_ex).
+ *          Q, O, dO and dQ use seq_q; K, V, dK and dV use seq_k. T is implied
+ *          by the offsets and never passed.
+ * The pages fix per-sample lengths n_q, n_k (rainbus.top summary, 方法步骤详情
+ * step 1) and say that cells are attended one by one, never split or
+ * concatenated with other cells (paperlayer.ai summary, section 1). The packed
+ * layout keeps exactly that per-sample attention: no score ever pairs rows of
+ * two samples. Only the storage changes, the valid rows back to back without
+ * padding rows; that storage variant is this library's own design, not the
+ * pages'. */
+typedef enum { SIGATTN_LAYOUT_PADDED = 0, SIGATTN_LAYOUT_PACKED = 1, SIGATTN_LAYOUT_INT_RANGE_ = 0x7fffffff } sigattn_layout;
 
 /* The score bias (paperlayer.ai summary, section 3: b = -log n).
  *  CONSTANT:   b = bias for every sample.
  *  NEG_LOG_NK: b_z = bias - ln(n_k[z]) for sample z (ln 1 for n_k = 0). With
  *              bias = 0 this is the per-sample reading b = -log(n). */
-typedef enum { SIGATTN_BIAS_CONSTANT = 0, SIGATTN_BIAS_NEG_LOG_NK = 1 } sigattn_bias_mode;
+typedef enum {
+  SIGATTN_BIAS_CONSTANT = 0,
+  SIGATTN_BIAS_NEG_LOG_NK = 1,
+  SIGATTN_BIAS_INT_RANGE_ = 0x7fffffff
+} sigattn_bias_mode;
 
 /* Which kernel a tile configuration or a counter refers to. */
-typedef enum { SIGATTN_KERNEL_FWD = 0, SIGATTN_KERNEL_DQ = 1, SIGATTN_KERNEL_DKDV = 2 } sigattn_kernel;
+typedef enum {
+  SIGATTN_KERNEL_FWD = 0,
+  SIGATTN_KERNEL_DQ = 1,
+  SIGATTN_KERNEL_DKDV = 2,
+  SIGATTN_KERNEL_INT_RANGE_ = 0x7fffffff
+} sigattn_kernel;
 
 /*
  * Forward: o = sigma(alpha * q k^T + bias) v with padding (rainbus.top summary,
@@ -97,8 +113,8 @@ typedef enum { SIGATTN_KERNEL_FWD = 0, SIGATTN_KERNEL_DQ = 1, SIGATTN_KERNEL_DKD
  *   o              [Z, L, H, D] output. Rows >= n_q[z] are written 0.
  *   seqlens_q/_k   int32[Z], device.
  *   alpha, bias    score scale and bias. The pages use 1/sqrt(D) and -log(n).
- *   workspace      device scratch of at least sigattn_workspace_size(FWD, ...)
- *                  bytes. May be NULL when that size is 0.
+ *   dtype          SIGATTN_BF16 or SIGATTN_FP32; any other value gives
+ *                  SIGATTN_EUNSUPPORTED.
  *   tile_counts    NULL, or int32[Z * H * ceil(L / BQ)], where BQ is the forward's
  *                  query tile from sigattn_tile_config. Entry (z, h, m) receives
  *                  the number of key tiles that query tile m computed. It is 0
@@ -106,8 +122,7 @@ typedef enum { SIGATTN_KERNEL_FWD = 0, SIGATTN_KERNEL_DQ = 1, SIGATTN_KERNEL_DKD
  */
 int sigattn_fwd(const void* q, const void* k, const void* v, void* o,
                 const int32_t* seqlens_q, const int32_t* seqlens_k,
-                int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                void* workspace, size_t workspace_bytes,
+                int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                 int32_t* tile_counts, void* stream);
 
 /*
@@ -125,8 +140,7 @@ int sigattn_fwd(const void* q, const void* k, const void* v, void* o,
 int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
                 void* dq, void* dk, void* dv,
                 const int32_t* seqlens_q, const int32_t* seqlens_k,
-                int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                void* workspace, size_t workspace_bytes,
+                int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                 int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
 
 /*
@@ -139,11 +153,11 @@ int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout,
  */
 int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
                      const int32_t* seqlens_q, const int32_t* seqlens_k,
-                     int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                     int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                      int32_t* tile_counts_dkdv, void* stream);
 int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                    const int32_t* seqlens_q, const int32_t* seqlens_k,
-                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                    int32_t* tile_counts_dq, void* stream);
 
 /*
@@ -156,31 +170,39 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
  */
 int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout, void* dk,
                    const int32_t* seqlens_q, const int32_t* seqlens_k,
-                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                    int32_t* tile_counts_dkdv, void* stream);
 int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv,
                    const int32_t* seqlens_q, const int32_t* seqlens_k,
-                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                    int32_t* tile_counts_dkdv, void* stream);
 
 /*
  * sigattn_fwd and sigattn_bwd with a choice of layout and bias mode (see
  * sigattn_layout and sigattn_bias_mode). With SIGATTN_LAYOUT_PADDED and
- * SIGATTN_BIAS_CONSTANT they are exactly sigattn_fwd and sigattn_bwd. In the
- * packed layout every row of every output belongs to a sample and is written;
- * tile counters are indexed as in the padded layout, with L tiles per (z, h).
+ * SIGATTN_BIAS_CONSTANT they are exactly sigattn_fwd and sigattn_bwd. Tile
+ * counters are indexed as in the padded layout, with ceil(L / tile) tiles per
+ * (z, h).
+ * Packed-layout contract, which the caller owns: the offsets live in device
+ * memory and the host never reads them (that would need a synchronisation),
+ * so they are not checked here. They must start at 0, never decrease, end at
+ * or below the tensors' row count T, and give no sample more than L rows.
+ * Under that contract every row of every output is written exactly once. A
+ * sample longer than L is cut at L: its rows past L are neither read nor
+ * written, so those output rows keep whatever they held. Offsets past T make
+ * the kernels read and write outside the tensors. (The Python binding checks
+ * all of this on the host before it calls in, and raises ValueError.)
  * Errors: as sigattn_fwd / sigattn_bwd, plus SIGATTN_EINVAL for an unknown
- * layout or bias mode. Lengths and offsets live in device memory and are not
- * checked on the host: offsets must be non-decreasing and within the tensors.
+ * layout or bias mode.
  */
 int sigattn_fwd_ex(const void* q, const void* k, const void* v, void* o,
-                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
-                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout, sigattn_bias_mode bias_mode,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                    int32_t* tile_counts, void* stream);
 int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout,
                    void* dq, void* dk, void* dv,
-                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
-                   int Z, int L, int H, int D, float alpha, float bias, int dtype,
+                   const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout, sigattn_bias_mode bias_mode,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
                    int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream);
 
 /*
@@ -217,13 +239,13 @@ int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout
  * lse or workspace, and SIGATTN_EWORKSPACE for a workspace that is too small.
  */
 int sigattn_softmax_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int32_t* seq_q, const int32_t* seq_k, int layout,
-                        int Z, int L, int H, int D, float alpha, int dtype, void* stream);
+                        const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout,
+                        int Z, int L, int H, int D, float alpha, sigattn_dtype dtype, void* stream);
 size_t sigattn_softmax_bwd_workspace_size(long long rows_q, int H);
 int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        const int32_t* seq_q, const int32_t* seq_k, int layout,
-                        int Z, int L, int H, int D, float alpha, int dtype,
+                        const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout,
+                        int Z, int L, int H, int D, float alpha, sigattn_dtype dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -250,21 +272,17 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
  * Errors: as sigattn_fwd_ex, plus SIGATTN_EINVAL for alpha <= 0, L > 262144
  * or a NULL scale array. Scale arrays need no alignment.
  */
-int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, int layout,
+int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, sigattn_layout layout,
                          int Z, int L, int H, int D, void* stream);
 int sigattn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                     const uint8_t* sq, const uint8_t* sk, const uint8_t* sv, void* o,
-                    const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode,
+                    const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout, sigattn_bias_mode bias_mode,
                     int Z, int L, int H, int D, float alpha, float bias, void* stream);
-
-/* Bytes of device workspace the forward (kernel == SIGATTN_KERNEL_FWD) or the
- * backward (any other value) needs for this shape. 0 means none. */
-size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype);
 
 /* The tile sizes a kernel uses, for reading the tile counters. block_q is the
  * query tile and block_k the key tile. Returns SIGATTN_EINVAL for an unknown
  * kernel, D or dtype. */
-int sigattn_tile_config(int kernel, int D, int dtype, int* block_q, int* block_k);
+int sigattn_tile_config(sigattn_kernel kernel, int D, sigattn_dtype dtype, int* block_q, int* block_k);
 
 /* A static description of a status code. */
 const char* sigattn_strerror(int status);

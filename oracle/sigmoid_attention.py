@@ -23,8 +23,13 @@ Models" (arXiv:2604.27124):
   sigma(x) = 1 / (1 + e^{-x}) and the forward sigma(Q K^T / sqrt(d) + b) V.
 * paperlayer.ai summary, section 3: the bias b = -log(n), taken either as one
   scalar for the batch or per sample, b_z = -log(n_k[z]).
-* The packed (varlen) layout: the samples' valid rows back to back, with
-  cumulative offsets, in place of padding (rainbus.top summary, "局限与改进").
+* Per-sample lengths (rainbus.top summary, "方法步骤详情" step 1), and cells
+  attended one by one, never split or concatenated with other cells
+  (paperlayer.ai summary, section 1). The packed (varlen) layout used by
+  forward_varlen and backward_varlen stores the samples' valid rows back to
+  back, with cumulative offsets, in place of padding. That storage variant is
+  this build's own; the pages do not describe it. Attention stays per sample,
+  so the results are those of the padded layout on the same valid rows.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 

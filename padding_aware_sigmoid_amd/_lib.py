@@ -33,7 +33,6 @@ EXPORTED_SYMBOLS = (
     "sigattn_softmax_bwd_workspace_size",
     "sigattn_quantize_fp8",
     "sigattn_fwd_fp8",
-    "sigattn_workspace_size",
     "sigattn_tile_config",
     "sigattn_strerror",
     "sigattn_last_error",
@@ -58,10 +57,9 @@ def load():
         raise SigattnError(f"{_LIB_PATH} is missing: build it first (python -m padding_aware_sigmoid_amd.build)")
     lib = ctypes.CDLL(str(_LIB_PATH))
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.sigattn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp, vp]
+    lib.sigattn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
     lib.sigattn_fwd.restype = i32
-    lib.sigattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp, vp,
-                                vp]
+    lib.sigattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp]
     lib.sigattn_bwd.restype = i32
     lib.sigattn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp]
     lib.sigattn_bwd_dkdv.restype = i32
@@ -87,8 +85,6 @@ def load():
     lib.sigattn_quantize_fp8.restype = i32
     lib.sigattn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.sigattn_fwd_fp8.restype = i32
-    lib.sigattn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
-    lib.sigattn_workspace_size.restype = sz
     lib.sigattn_tile_config.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.sigattn_tile_config.restype = i32
     lib.sigattn_strerror.argtypes = [i32]
@@ -113,10 +109,6 @@ def tile_config(kernel: int, D: int, dtype: int):
     bq, bk = ctypes.c_int(), ctypes.c_int()
     check(lib.sigattn_tile_config(kernel, D, dtype, ctypes.byref(bq), ctypes.byref(bk)))
     return bq.value, bk.value
-
-
-def workspace_size(kernel: int, Z: int, L: int, H: int, D: int, dtype: int) -> int:
-    return int(load().sigattn_workspace_size(kernel, Z, L, H, D, dtype))
 
 
 def version() -> str:

@@ -87,10 +87,12 @@ int check_common(int Z, int L, int H, int D, float alpha, float bias, int dtype,
   if (!std::isfinite(alpha) || !std::isfinite(bias)) return fail(SIGATTN_EINVAL, "alpha and bias must be finite%s");
   if (Z == 0 || L == 0 || H == 0) return 1;
   if (nq == nullptr || nk == nullptr) return fail(SIGATTN_EINVAL, "seqlens_q and seqlens_k must not be NULL%s");
-  // The largest grid is Z * H * ceil(L / 256) blocks of 256 work-items (the
-  // fp32 kernels' 64-row tiles of 64 work-items need no more), and a dispatch
-  // holds at most 2^32 - 1 work-items. Element offsets are 64-bit.
-  const long long items = (long long)Z * H * ((L + 255) / 256) * 256;
+  // The largest grid has one workgroup of 256 work-items per 128 rows of each
+  // (sample, head) pair: the fused dK/dV kernel and the exchanged sigmoid dQ
+  // at D = 64 own 128 rows per workgroup, every other bf16 kernel 256, and
+  // the fp32 kernels 64 rows per workgroup of 64 work-items. A dispatch holds
+  // at most 2^32 - 1 work-items. Element offsets are 64-bit.
+  const long long items = (long long)Z * H * ((L + 127) / 128) * 256;
   if (items > 0xffffffffLL) return fail(SIGATTN_EINVAL, "problem too large for one grid%s");
   // Tiles reach LDS through buffer loads with 32-bit offsets below 256 rows.
   if ((long long)H * D * 2 * 256 >= 0x80000000LL) return fail(SIGATTN_EINVAL, "H * D too large%s");
@@ -176,17 +178,15 @@ int check_modes(int layout, int bias_mode) {
 extern "C" {
 
 int sigattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* seqlens_q,
-                const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                void* workspace, size_t workspace_bytes, int32_t* tile_counts, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
+                int32_t* tile_counts, void* stream) {
   return sigattn_fwd_ex(q, k, v, o, seqlens_q, seqlens_k, SIGATTN_LAYOUT_PADDED, SIGATTN_BIAS_CONSTANT, Z, L, H, D,
                         alpha, bias, dtype, tile_counts, stream);
 }
 
 int sigattn_fwd_ex(const void* q, const void* k, const void* v, void* o, const int32_t* seq_q, const int32_t* seq_k,
-                   int layout, int bias_mode, int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                   int32_t* tile_counts, void* stream) {
+                   sigattn_layout layout, sigattn_bias_mode bias_mode, int Z, int L, int H, int D, float alpha,
+                   float bias, sigattn_dtype dtype, int32_t* tile_counts, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, bias_mode);
   if (rc != 0) return rc;
@@ -201,19 +201,16 @@ int sigattn_fwd_ex(const void* q, const void* k, const void* v, void* o, const i
 
 int sigattn_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
                 const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
-                float bias, int dtype, void* workspace, size_t workspace_bytes, int32_t* tile_counts_dq,
-                int32_t* tile_counts_dkdv, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                float bias, sigattn_dtype dtype, int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream) {
   return sigattn_bwd_ex(q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_k, SIGATTN_LAYOUT_PADDED,
                         SIGATTN_BIAS_CONSTANT, Z, L, H, D, alpha, bias, dtype, tile_counts_dq, tile_counts_dkdv,
                         stream);
 }
 
 int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                   const int32_t* seq_q, const int32_t* seq_k, int layout, int bias_mode, int Z, int L, int H, int D,
-                   float alpha, float bias, int dtype, int32_t* tile_counts_dq, int32_t* tile_counts_dkdv,
-                   void* stream) {
+                   const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout, sigattn_bias_mode bias_mode,
+                   int Z, int L, int H, int D, float alpha, float bias, sigattn_dtype dtype,
+                   int32_t* tile_counts_dq, int32_t* tile_counts_dkdv, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, bias_mode);
   if (rc != 0) return rc;
@@ -232,7 +229,7 @@ int sigattn_bwd_ex(const void* q, const void* k, const void* v, const void* dout
 
 int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
                      const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
-                     float bias, int dtype, int32_t* tile_counts_dkdv, void* stream) {
+                     float bias, sigattn_dtype dtype, int32_t* tile_counts_dkdv, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
@@ -245,7 +242,7 @@ int sigattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* do
 
 int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout, void* dk,
                    const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
-                   float bias, int dtype, int32_t* tile_counts_dkdv, void* stream) {
+                   float bias, sigattn_dtype dtype, int32_t* tile_counts_dkdv, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
@@ -257,8 +254,8 @@ int sigattn_bwd_dk(const void* q, const void* k, const void* v, const void* dout
 }
 
 int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv, const int32_t* seqlens_q,
-                   const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias, int dtype,
-                   int32_t* tile_counts_dkdv, void* stream) {
+                   const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha, float bias,
+                   sigattn_dtype dtype, int32_t* tile_counts_dkdv, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
@@ -271,7 +268,7 @@ int sigattn_bwd_dv(const void* q, const void* k, const void* dout, void* dv, con
 
 int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                    const int32_t* seqlens_q, const int32_t* seqlens_k, int Z, int L, int H, int D, float alpha,
-                   float bias, int dtype, int32_t* tile_counts_dq, void* stream) {
+                   float bias, sigattn_dtype dtype, int32_t* tile_counts_dq, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_common(Z, L, H, D, alpha, bias, dtype, seqlens_q, seqlens_k);
   if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
@@ -283,8 +280,8 @@ int sigattn_bwd_dq(const void* q, const void* k, const void* v, const void* dout
 }
 
 int sigattn_softmax_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* seq_q,
-                        const int32_t* seq_k, int layout, int Z, int L, int H, int D, float alpha, int dtype,
-                        void* stream) {
+                        const int32_t* seq_k, sigattn_layout layout, int Z, int L, int H, int D, float alpha,
+                        sigattn_dtype dtype, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
   if (rc != 0) return rc;
@@ -313,8 +310,8 @@ size_t sigattn_softmax_bwd_workspace_size(long long rows_q, int H) {
 
 int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, const int32_t* seq_q, const int32_t* seq_k,
-                        int layout, int Z, int L, int H, int D, float alpha, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        sigattn_layout layout, int Z, int L, int H, int D, float alpha, sigattn_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
   if (rc != 0) return rc;
@@ -355,8 +352,8 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
   return hip_status(e);
 }
 
-int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, int layout, int Z, int L,
-                         int H, int D, void* stream) {
+int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, sigattn_layout layout,
+                         int Z, int L, int H, int D, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
   if (rc != 0) return rc;
@@ -371,8 +368,8 @@ int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t
 }
 
 int sigattn_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* sq, const uint8_t* sk,
-                    const uint8_t* sv, void* o, const int32_t* seq_q, const int32_t* seq_k, int layout,
-                    int bias_mode, int Z, int L, int H, int D, float alpha, float bias, void* stream) {
+                    const uint8_t* sv, void* o, const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout,
+                    sigattn_bias_mode bias_mode, int Z, int L, int H, int D, float alpha, float bias, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_modes(layout, bias_mode);
   if (rc != 0) return rc;
@@ -391,17 +388,7 @@ int sigattn_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_
                             : sigattn::launch_fwd_fp8<128>(q8, k8, v8, sq, sk, sv, o, sl, Z, H, c1, c0, st));
 }
 
-size_t sigattn_workspace_size(int kernel, int Z, int L, int H, int D, int dtype) {
-  (void)kernel;
-  (void)Z;
-  (void)L;
-  (void)H;
-  (void)D;
-  (void)dtype;
-  return 0;
-}
-
-int sigattn_tile_config(int kernel, int D, int dtype, int* block_q, int* block_k) {
+int sigattn_tile_config(sigattn_kernel kernel, int D, sigattn_dtype dtype, int* block_q, int* block_k) {
   if (block_q == nullptr || block_k == nullptr || (D != 64 && D != 128)) return SIGATTN_EINVAL;
   return tile_config(kernel, dtype, block_q, block_k) ? SIGATTN_OK : SIGATTN_EINVAL;
 }

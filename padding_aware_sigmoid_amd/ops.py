@@ -72,14 +72,6 @@ def _bias_mode(mode) -> int:
     return int(mode)
 
 
-def _workspace(kernel: int, q: torch.Tensor):
-    Z, L, H, D = q.shape
-    nbytes = _lib.workspace_size(kernel, Z, L, H, D, _dtype_code(q))
-    if nbytes == 0:
-        return None, 0
-    return torch.empty(nbytes, dtype=torch.uint8, device=q.device), nbytes
-
-
 def sigattn_fwd(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, out=None, tile_counts=None,
                 bias_mode="constant"):
     """O = sigma(alpha q k^T + b) v with padding. Wraps the C entry point sigattn_fwd
@@ -101,10 +93,8 @@ def sigattn_fwd(q, k, v, seqlens_q, seqlens_k, alpha=None, bias=None, out=None, 
     lib = _lib.load()
     tc = None if tile_counts is None else tile_counts.data_ptr()
     if mode == _lib.BIAS_CONSTANT:
-        ws, wsb = _workspace(_lib.KERNEL_FWD, q)
         _lib.check(lib.sigattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(),
-                                   nk.data_ptr(), Z, L, H, D, alpha, bias, _dtype_code(q),
-                                   None if ws is None else ws.data_ptr(), wsb, tc, _stream(q.device)))
+                                   nk.data_ptr(), Z, L, H, D, alpha, bias, _dtype_code(q), tc, _stream(q.device)))
     else:
         _lib.check(lib.sigattn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nq.data_ptr(),
                                       nk.data_ptr(), _lib.LAYOUT_PADDED, mode, Z, L, H, D, alpha, bias,
@@ -129,10 +119,9 @@ def sigattn_bwd(q, k, v, dout, seqlens_q, seqlens_k, alpha=None, bias=None, dq=N
     lib = _lib.load()
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     if mode == _lib.BIAS_CONSTANT:
-        ws, wsb = _workspace(_lib.KERNEL_DQ, q)
         _lib.check(lib.sigattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
                                    dk.data_ptr(), dv.data_ptr(), nq.data_ptr(), nk.data_ptr(), Z, L, H, D, alpha,
-                                   bias, _dtype_code(q), ptr(ws), wsb, ptr(tile_counts_dq), ptr(tile_counts_dkdv),
+                                   bias, _dtype_code(q), ptr(tile_counts_dq), ptr(tile_counts_dkdv),
                                    _stream(q.device)))
     else:
         _lib.check(lib.sigattn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
@@ -165,6 +154,28 @@ def _offsets(cu, device) -> torch.Tensor:
     return t.to(device).contiguous()
 
 
+def check_offsets(cu, rows: int, max_len: int, name: str = "cu_seqlens") -> None:
+    """The packed layout's contract, checked on the host: offsets start at 0,
+    never decrease, end at or below the tensor's row count, and give no sample
+    more than max_len rows. The kernels read the offsets from device memory and
+    trust them (an offset past the tensor would make them read and write out of
+    bounds; a sample longer than max_len would leave its rows past max_len
+    unwritten), so every packed entry point calls this first. A device tensor
+    is copied to the host for the check, which synchronises with its stream."""
+    c = (cu.detach().cpu() if isinstance(cu, torch.Tensor) else torch.as_tensor(cu)).to(torch.int64).reshape(-1)
+    if c.numel() < 1:
+        raise ValueError(f"{name} must hold Z + 1 offsets")
+    if int(c[0]) != 0:
+        raise ValueError(f"{name} must start at 0, got {int(c[0])}")
+    d = c[1:] - c[:-1]
+    if d.numel() and int(d.min()) < 0:
+        raise ValueError(f"{name} must be non-decreasing")
+    if int(c[-1]) > rows:
+        raise ValueError(f"{name} ends at {int(c[-1])}, past the tensor's {rows} rows")
+    if d.numel() and int(d.max()) > max_len:
+        raise ValueError(f"{name}: a sample has {int(d.max())} rows, more than max_len = {max_len}")
+
+
 def sigattn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None, bias=None, out=None,
                        tile_counts=None, bias_mode="constant"):
     """Sigmoid attention over packed sequences. Wraps sigattn_fwd_ex with the packed layout.
@@ -179,6 +190,8 @@ def sigattn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_len, alpha=None,
     if cq.numel() != ck.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
     Z, L = cq.numel() - 1, int(max_len)
+    check_offsets(cq, q.shape[0], L, "cu_seqlens_q")
+    check_offsets(ck, k.shape[0], L, "cu_seqlens_k")
     mode = _bias_mode(bias_mode)
     alpha = default_alpha(D) if alpha is None else float(alpha)
     bias = default_bias(max(L, 1), mode) if bias is None else float(bias)
@@ -200,6 +213,8 @@ def sigattn_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, max_len, alpha
     if cq.numel() != ck.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
     Z, L = cq.numel() - 1, int(max_len)
+    check_offsets(cq, q.shape[0], L, "cu_seqlens_q")
+    check_offsets(ck, k.shape[0], L, "cu_seqlens_k")
     mode = _bias_mode(bias_mode)
     alpha = default_alpha(D) if alpha is None else float(alpha)
     bias = default_bias(max(L, 1), mode) if bias is None else float(bias)
@@ -364,6 +379,8 @@ def _softmax_layout(q, k, seq_q, seq_k, max_len, named_q: dict, named_k: dict):
     cq, ck = _offsets(seq_q, q.device), _offsets(seq_k, q.device)
     if cq.numel() != ck.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold Z + 1 offsets")
+    check_offsets(cq, q.shape[0], int(max_len), "cu_seqlens_q")
+    check_offsets(ck, k.shape[0], int(max_len), "cu_seqlens_k")
     return _lib.LAYOUT_PACKED, cq.numel() - 1, int(max_len), cq, ck
 
 
@@ -473,6 +490,7 @@ def _fp8_layout(x, seq, max_len):
     if max_len is None:
         raise ValueError("packed [T, H, D] tensors need max_len")
     cu = _offsets(seq, x.device)
+    check_offsets(cu, x.shape[0], int(max_len))
     return _lib.LAYOUT_PACKED, cu.numel() - 1, int(max_len), cu
 
 

@@ -133,13 +133,13 @@ def test_empty_and_errors():
     x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16, device="cuda")
     n = torch.full((1,), 8, dtype=torch.int32, device="cuda")
     p = x.data_ptr()
-    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 96, 1.0, 0.0, 0, None, 0, None, None) == -1
-    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 7, None, 0, None, None) == -2
-    assert lib.sigattn_fwd(None, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None, 0, None,
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 96, 1.0, 0.0, 0, None, None) == -1
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 7, None, None) == -2
+    assert lib.sigattn_fwd(None, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None,
                            None) == -1
-    assert lib.sigattn_fwd(p + 2, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None, 0, None,
+    assert lib.sigattn_fwd(p + 2, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, 1.0, 0.0, 0, None,
                            None) == -1
-    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, float("nan"), 0.0, 0, None, 0, None,
+    assert lib.sigattn_fwd(p, p, p, p, n.data_ptr(), n.data_ptr(), 1, 8, 1, 64, float("nan"), 0.0, 0, None,
                            None) == -1
     torch.cuda.synchronize()
     # Outputs are fully written even where the caller left garbage in them.
