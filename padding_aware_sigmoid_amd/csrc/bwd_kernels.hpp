@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
     }
   }
 
-  const int nkt = (nk + C::BK_DQ - 1) / C::BK_DQ;
-  const int nkt3 = (nkt + 2) / 3 * 3;
+  const int nkt = (nk + C::BK_DQ - 1) / C::BK_DQ;  // live key tiles; no other tile is computed
+  int executed = 0;                                 // key tiles whose scores this workgroup computed
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Kb = K + base_k;
@@ -148,48 +148,58 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
           acc[1][db] = mfma32(dsp[1][ks], b, acc[1][db]);
         }
     };
-    // dS of the previous 32-key block, waiting for its dQ MFMAs (zero before the first block).
-    bf16x8 ds_prev[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) ds_prev[qb][0] = ds_prev[qb][1] = zero_bf16x8();
-    // One key tile in slot S; slot P holds the tile before it, slot N receives
-    // the next. The tile's two 32-key blocks run as one stream of steps, each
-    // one LDS read and two MFMAs (one per query block):
+    // dS of the previous 32-key block (block 1 of the previous tile), waiting
+    // for its dQ MFMAs; dS of block 0 of the current tile, for block 1's.
+    bf16x8 ds_prev[2][2], ds_mid[2][2];
+    // Each key tile is two 32-key blocks. Block 0 of tile t: S^T, dP^T, then
+    // the dQ MFMAs of block 1 of tile t-1 beside sigma and dS. Block 1: S^T,
+    // dP^T, then the dQ of block 0 of the same tile. The key loop runs block 1
+    // of tile t and block 0 of tile t+1 per body, so each body adds exactly
+    // one key tile (t+1). The prologue is block 0 of tile 0 (there is no
+    // tile -1 to take dQ from) and the epilogue block 1 of the last tile plus
+    // its dQ.
+    //
+    // At D = 128 a block runs as one explicit stream of steps, each one LDS
+    // read and two MFMAs (one per query block):
     //   block steps 0 .. KS - 1: S^T of this block (K read by rows);
     //   block steps KS .. 2 KS - 1: dP^T of this block (V read by rows), beside
     //     P = sigma(S), written over the scores;
     //   block steps 2 KS .. 2 KS + 2 NB - 1: dQ += dS K of the previous block
     //     (K read transposed), beside dS of this block.
-    // Each step's operand is read two steps ahead, across the block boundary.
+    // Each step's operand is read two steps ahead, from block 0 into block 1;
+    // block 0's first two reads follow the barrier that publishes its tile.
     // Splitting sigma from dS this way spreads the VALU work over two thirds of
     // the steps instead of one third: 1% faster than all of it beside dQ.
+    // sk, sv: this block's tile; skq: the tile whose block (1 - BLK) the dQ
+    // MFMAs read (the previous tile for block 0, the same tile for block 1).
     constexpr int NA = 2 * C::KS, NSB = NA + 2 * C::NB, NT = 2 * NSB;
     constexpr int NE = 32;  // scores per lane and block: two query blocks of 16
-    auto iteration_stream = [&](auto s_c, auto p_c, auto n_c, int t) {
-      constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      const __bf16* const sk = ring<S>(sK0, sK1, sK2);
-      const __bf16* const sv = ring<S>(sV0, sV1, sV2);
-      const __bf16* const skp = ring<P>(sK0, sK1, sK2);
-      dma_wait();
-      __syncthreads();  // tile t is in LDS, and every wave is done with iteration t-1
-      if (t + 1 < nkt3) fetch(ring<N>(sK0, sK1, sK2), ring<N>(sV0, sV1, sV2), t + 1);  // slot N held tile t-2
+    bf16x8 ops[3];
+    auto block_stream = [&](auto blk_c, auto nodq_c, const __bf16* sk, const __bf16* sv,
+                            const __bf16* skq) __attribute__((always_inline)) {
+      constexpr int BLK = decltype(blk_c)::value;
+      constexpr bool NO_DQ = decltype(nodq_c)::value;
       auto read = [&](auto gc) -> bf16x8 {
         constexpr int g = decltype(gc)::value, blk = g / NSB, j = g % NSB;
         if constexpr (j < NA) {
           return lds_nat<D>(j >= C::KS ? sv : sk, blk * 32 + l32, 2 * (j % C::KS) + half);
         } else {
           constexpr int i = j - NA, db = i >> 1, ks = i & 1;
-          return lds_tr<D>(blk == 0 ? skp : sk, (1 - blk) * 32 + ks * 16, db * 32, lane);
+          return lds_tr<D>(skq, (1 - blk) * 32 + ks * 16, db * 32, lane);
         }
       };
       f32x16 sacc[2], pacc[2];
-      bf16x8 ds_mid[2][2];  // dS of block 0, for block 1's dQ
-      bf16x8 ops[3];
-      ops[0] = read(std::integral_constant<int, 0>{});
-      ops[1] = read(std::integral_constant<int, 1>{});
-      static_for<0, NT>([&](auto gc) {
+      if constexpr (BLK == 0) {
+        ops[0] = read(std::integral_constant<int, 0>{});
+        ops[1] = read(std::integral_constant<int, 1>{});
+      }
+      static_for<BLK * NSB, BLK * NSB + NSB>([&](auto gc) {
         constexpr int g = decltype(gc)::value, blk = g / NSB, j = g % NSB;
-        if constexpr (g + 2 < NT) ops[(g + 2) % 3] = read(std::integral_constant<int, g + 2>{});
+        // the read two steps ahead: none into the dQ steps of a block without
+        // them, none past the tile (block 0 of the next tile follows a barrier)
+        constexpr int ga = g + 2;
+        constexpr bool skip_ahead = ga >= NT || (NO_DQ && ga / NSB == BLK && ga % NSB >= NA);
+        if constexpr (!skip_ahead) ops[ga % 3] = read(std::integral_constant<int, ga>{});
         const bf16x8 op = ops[g % 3];
         if constexpr (j == 0) {
 #pragma unroll
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
             else
               sacc[qb] = mfma32(op, qf[qb][s], sacc[qb]);
           }
-        } else {
+        } else if constexpr (!NO_DQ) {
           constexpr int i = j - NA, db = i >> 1, ks = i & 1;
           const bf16x8 (&dsB)[2][2] = blk == 0 ? ds_prev : ds_mid;
 #pragma unroll
@@ -234,58 +244,48 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
           else
             dsV[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - st[qb].y));
         });
-        constexpr int nds = g + 2 < NT ? ((g + 2) % NSB < NA ? 1 : 2) : 0;
+        constexpr int nds = skip_ahead ? 0 : ((ga % NSB) < NA ? 1 : 2);
         constexpr int nvalu = (p1 - p0) * (ACT == ACT_SIGMOID ? 4 : 2) + (d1 - d0) * 3;
-        sched_step<g, nds, 2, nvalu, 1>();
+        sched_step<g, nds, (NO_DQ && j >= NA) ? 0 : 2, nvalu, 1>();
       });
     };
-    // The same tile in plain loops (D = 64): S^T and dP^T of a block, then the
-    // previous block's dQ MFMAs beside this block's sigma and dS, scheduled by
-    // the compiler.
-    auto iteration_plain = [&](auto s_c, auto p_c, auto n_c, int t) {
-      constexpr int S = decltype(s_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      __bf16* const sk = ring<S>(sK0, sK1, sK2);
-      __bf16* const sv = ring<S>(sV0, sV1, sV2);
-      const __bf16* const skp = ring<P>(sK0, sK1, sK2);
-      dma_wait();
-      __syncthreads();  // tile t is in LDS, and every wave is done with iteration t-1
-      if (t + 1 < nkt3) fetch(ring<N>(sK0, sK1, sK2), ring<N>(sV0, sV1, sV2), t + 1);  // slot N held tile t-2
+    // The same block in plain loops (D = 64): S^T and dP^T, then the dQ
+    // MFMAs of the previous block beside this block's sigma and dS, scheduled
+    // by the compiler.
+    auto block_plain = [&](auto blk_c, auto nodq_c, const __bf16* sk, const __bf16* sv,
+                           const __bf16* skq) __attribute__((always_inline)) {
+      constexpr int BLK = decltype(blk_c)::value;
+      constexpr bool NO_DQ = decltype(nodq_c)::value;
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T, dP^T for this block (32 MFMAs)
-        f32x16 sacc[2], pacc[2];
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[qb][r] = pacc[qb][r] = 0.0f;
+      for (int s = 0; s < C::KS; ++s) {
+        const bf16x8 ak = lds_nat<D>(sk, BLK * 32 + l32, 2 * s + half);
+        const bf16x8 av = lds_nat<D>(sv, BLK * 32 + l32, 2 * s + half);
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 ak = lds_nat<D>(sk, kb * 32 + l32, 2 * s + half);
-          const bf16x8 av = lds_nat<D>(sv, kb * 32 + l32, 2 * s + half);
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[qb] = mfma32(ak, qf[qb][s], sacc[qb]);
+          pacc[qb] = mfma32(av, dof[qb][s], pacc[qb]);
+        }
+      }
+      if constexpr (!NO_DQ) dq_mfmas(skq, 1 - BLK, BLK == 0 ? ds_prev : ds_mid);
+      bf16x8 (&dsV)[2][2] = BLK == 0 ? ds_mid : ds_prev;
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            sacc[qb] = mfma32(ak, qf[qb][s], sacc[qb]);
-            pacc[qb] = mfma32(av, dof[qb][s], pacc[qb]);
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (ACT == ACT_SIGMOID) {
+            const float p = sigmoid_dot(sacc[qb][r], c1, c0);
+            dsV[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
+          } else {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c1, -st[qb].x));
+            dsV[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - st[qb].y));
           }
         }
-        if (kb == 0)
-          dq_mfmas(skp, 1, ds_prev);
-        else
-          dq_mfmas(sk, 0, ds_prev);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if constexpr (ACT == ACT_SIGMOID) {
-              const float p = sigmoid_dot(sacc[qb][r], c1, c0);
-              ds_prev[qb][r >> 3][r & 7] = (__bf16)(__builtin_fmaf(-p, p, p) * pacc[qb][r]);
-            } else {
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c1, -st[qb].x));
-              ds_prev[qb][r >> 3][r & 7] = (__bf16)(p * (pacc[qb][r] - st[qb].y));
-            }
-          }
-        interleave_mfma_valu<4 * C::KS + 2 * C::NB * 2, 6>();
-      }
+      interleave_mfma_valu<4 * C::KS + (NO_DQ ? 0 : 2 * C::NB * 2), 6>();
     };
     // At D = 128 the explicit step stream keeps each LDS read four MFMAs ahead
     // of its use; in plain loops the compiler leaves a third of the reads right
@@ -294,28 +294,57 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
     // sigmoid takes the swapped dK/dV kernel) the stream spills 47 registers
     // and the softmax backward ran 16% slower on cellbatch8k, so it keeps the
     // plain loops.
-    auto iteration = [&](auto s_c, auto p_c, auto n_c, int t) {
+    auto block = [&](auto blk_c, auto nodq_c, const __bf16* sk, const __bf16* sv,
+                     const __bf16* skq) __attribute__((always_inline)) {
       if constexpr (D == 128)
-        iteration_stream(s_c, p_c, n_c, t);
+        block_stream(blk_c, nodq_c, sk, sv, skq);
       else
-        iteration_plain(s_c, p_c, n_c, t);
+        block_plain(blk_c, nodq_c, sk, sv, skq);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // Slot 2 stands in for tile -1: its reads are multiplied by ds_prev = 0, so
-    // it must hold finite values. It starts as zeros.
-    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sK2 + c * 8) = zero_bf16x8();
-    // The loop runs a multiple of three tiles. Tiles past n_k arrive as zeros
-    // (every DMA lane is out of range); a zero V row gives dP = 0 and so dS = 0,
-    // so they add exactly nothing.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using DQ = std::false_type;
+    using NODQ = std::true_type;
+    // Tile t sits in slot t mod 3. Tile 0, then tile 1 behind block 0 of tile 0.
     fetch(sK0, sV0, 0);
-    for (int t = 0; t < nkt3; t += 3) {
-      iteration(I0{}, I2{}, I1{}, t);
-      iteration(I1{}, I0{}, I2{}, t + 1);
-      iteration(I2{}, I1{}, I0{}, t + 2);
+    dma_wait();
+    __syncthreads();
+    if (nkt > 1) fetch(lds_opaque(sK1), lds_opaque(sV1), 1);  // waited for at the first body's barrier
+    block(B0{}, NODQ{}, sK0, sV0, sK0);
+    executed = 1;
+    // Body for tile t in slot T (tile t+1 in slot N; slot P held tile t-1 and
+    // receives tile t+2): block 1 of tile t, the barrier (tile t+1 is in LDS,
+    // every wave is done with slot P), then block 0 of tile t+1.
+    auto body = [&](const __bf16* kT, const __bf16* vT, __bf16* kN, __bf16* vN, __bf16* kP, __bf16* vP,
+                    int t) __attribute__((always_inline)) {
+      block(B1{}, DQ{}, kT, vT, kT);
+      dma_wait();
+      __syncthreads();
+      if (t + 2 < nkt) fetch(kP, vP, t + 2);
+      block(B0{}, DQ{}, kN, vN, kT);
+      ++executed;
+    };
+    // Whole rounds of three bodies, then the one or two left over, with their
+    // slots through lds_opaque: named at compile time they made the compiler
+    // rebuild the loop's LDS addresses; opaque, it also leaves their DMA to
+    // the explicit dma_wait and barrier of the next body.
+    const int nb = nkt - 1, nb3 = nb / 3 * 3;
+    for (int t = 0; t < nb3; t += 3) {
+      body(sK0, sV0, sK1, sV1, sK2, sV2, t);
+      body(sK1, sV1, sK2, sV2, sK0, sV0, t + 1);
+      body(sK2, sV2, sK0, sV0, sK1, sV1, t + 2);
     }
-    dq_mfmas(sK2, 1, ds_prev);  // the last block, of tile nkt3 - 1 (slot 2)
+    if (nb3 < nb)
+      body(lds_opaque(sK0), lds_opaque(sV0), lds_opaque(sK1), lds_opaque(sV1), lds_opaque(sK2), lds_opaque(sV2), nb3);
+    if (nb3 + 1 < nb)
+      body(lds_opaque(sK1), lds_opaque(sV1), lds_opaque(sK2), lds_opaque(sV2), lds_opaque(sK0), lds_opaque(sV0),
+           nb3 + 1);
+    // Epilogue: block 1 of the last tile (slot nb mod 3), then its dQ.
+    const int last = nb - nb3;
+    const __bf16* kL = lds_opaque(last == 0 ? sK0 : (last == 1 ? sK1 : sK2));
+    const __bf16* vL = lds_opaque(last == 0 ? sV0 : (last == 1 ? sV1 : sV2));
+    block(B1{}, DQ{}, kL, vL, kL);
+    dq_mfmas(kL, 1, ds_prev);
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -326,7 +355,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
         const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
         if (row < rows) dQb[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? alpha * acc[qb][db][r] : 0.0f);
       }
-  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
+  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = executed;
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
@@ -584,7 +613,8 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
   constexpr int KB = SWAP ? 1 : kKB<D, MODE>;
   constexpr int WK = 32 * KB;           // keys per wave
   static_assert(C::NWAVE * WK == KT, "the workgroup's waves cover its keys");
-  const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;
+  const int nqt = (nq + C::BQ_KV - 1) / C::BQ_KV;  // live query tiles; no other tile is computed
+  int executed = 0;                                 // query tiles whose A stage ran (the prologue and each iteration)
   // One pass over the query tiles for the workgroup's keys kh .. kh + KT - 1.
   // The loop runs once. Written as a plain block instead, the same code
   // compiled to 502 registers instead of 459 (fused kernel, D = 128), 56
@@ -638,6 +668,7 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
                                                 ptY, dsY, sY, pY, kf, vf, c1, c0, s_cur, l32, half, lane);
         kv_step<D, MODE, ACT, true, true, true, KB>(q_cur, g_cur, 1, q_prev, g_prev, 1, sY, pY, dkacc, dvacc, ptY, dsY,
                                                 ptX, dsX, sX, pX, kf, vf, c1, c0, s_cur, l32, half, lane);
+        ++executed;
       };
       // Tile 0 into slot 0, then tile 1 into slot 1 (q1, g1, s1: its DMA
       // destinations) behind the first A stages.
@@ -650,6 +681,7 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
                                                   pY, kf, vf, c1, c0, s0, l32, half, lane);
         kv_step<D, MODE, ACT, true, false, true, KB>(q0, g0, 1, q0, g0, 0, sY, pY, dkacc, dvacc, ptY, dsY, ptX, dsX, sX,
                                                  pX, kf, vf, c1, c0, s0, l32, half, lane);
+        executed = 1;
       };
       auto epilogue = [&](__bf16* q_last, __bf16* g_last, float2* s_last) {
         kv_step<D, MODE, ACT, false, true, true, KB>(q_last, g_last, 0, q_last, g_last, 0, sX, pX, dkacc, dvacc, ptX,
@@ -658,17 +690,33 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
                                                   dsY, ptX, dsX, sX, pX, kf, vf, c1, c0, s_last, l32, half, lane);
       };
       if constexpr (UR) {
-        // A multiple of three tiles after tile 0. Tiles past n_q arrive as zeros
-        // (every DMA lane is out of range): zero dO rows give dP = 0, so they add
-        // exactly nothing to dV or dK.
-        const int nqt3 = 1 + (nqt + 1) / 3 * 3;
-        prologue(sQ0, sG0, sS0, sQ1, sG1, sS1, nqt3);
-        for (int u = 1; u < nqt3; u += 3) {
-          iteration(sQ1, sG1, sS1, sQ0, sG0, sQ2, sG2, sS2, u, nqt3);
-          iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt3);
-          iteration(sQ0, sG0, sS0, sQ2, sG2, sQ1, sG1, sS1, u + 2, nqt3);
+        // Query tile u sits in slot u mod 3. Exactly the nqt live tiles run:
+        // tile 0 in the prologue, tiles 1 .. nqt-1 in the iterations (whole
+        // rounds of three, then the one or two left over), and the last
+        // tile's B and V stages in the epilogue. A loop entered or left in the
+        // middle of a round makes the compiler spill heavily, so the leftover
+        // iterations sit after it.
+        prologue(sQ0, sG0, sS0, sQ1, sG1, sS1, nqt);
+        const int ni = nqt - 1, ni3 = ni / 3 * 3;
+        for (int u = 1; u <= ni3; u += 3) {
+          iteration(sQ1, sG1, sS1, sQ0, sG0, sQ2, sG2, sS2, u, nqt);
+          iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt);
+          iteration(sQ0, sG0, sS0, sQ2, sG2, sQ1, sG1, sS1, u + 2, nqt);
         }
-        epilogue(sQ0, sG0, sS0);  // tile nqt3 - 1 sits in slot 0
+        // The leftover iterations take their slots through lds_opaque: the
+        // compiler then neither shares their LDS addresses with the loop's
+        // (sharing them cost the loop 40 address adds per round) nor waits
+        // for their DMA on its own; each iteration waits for it itself
+        // (dma_wait and the barrier at its top).
+        auto o = [](auto* x) { return lds_opaque(x); };
+        if (ni3 < ni) iteration(o(sQ1), o(sG1), o(sS1), o(sQ0), o(sG0), o(sQ2), o(sG2), o(sS2), ni3 + 1, nqt);
+        if (ni3 + 1 < ni) iteration(o(sQ2), o(sG2), o(sS2), o(sQ1), o(sG1), o(sQ0), o(sG0), o(sS0), ni3 + 2, nqt);
+        // The last tile's B and V stages, in its slot (nqt - 1) mod 3, named at
+        // compile time: with a runtime-selected slot the compiler also
+        // rebuilt the loop's LDS addresses (40 more address adds per round).
+        const int last = ni % 3;  // the slot of tile nqt - 1
+        epilogue(last == 0 ? sQ0 : (last == 1 ? sQ1 : sQ2), last == 0 ? sG0 : (last == 1 ? sG1 : sG2),
+                 last == 0 ? sS0 : (last == 1 ? sS1 : sS2));
       } else {
         // The three slots are parts of one array, indexed at run time. Every
         // read names that array, so the compiler can match it against DMAs.
@@ -705,7 +753,7 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
           }
         }
   }
-  if (tile_counts != nullptr && tid == 0 && t % WPT == 0) tile_counts[((size_t)z * H + h) * n_kt + t / WPT] = nqt;
+  if (tile_counts != nullptr && tid == 0 && t % WPT == 0) tile_counts[((size_t)z * H + h) * n_kt + t / WPT] = executed;
 }
 
 // The softmax dK kernel at D = 128 lives in its own translation unit, built

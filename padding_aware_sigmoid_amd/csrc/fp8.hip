@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const __bf16* __restr
 
 // ---------------------------------------------------------------------------------------- forward
 template <int D>
-__global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+__global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                       const uint8_t* __restrict__ V, const uint8_t* __restrict__ sQ,
                                                       const uint8_t* __restrict__ sK, const uint8_t* __restrict__ sV,
                                                       __bf16* __restrict__ O, SeqLayout sl, int Z, int H, float c1,
@@ -272,10 +272,10 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
 
+  // Exactly the key tiles below n_k are computed, each once: tile 0's scores
+  // in the prologue, then one iteration per tile, the last of which computes
+  // no next-tile scores.
   const int nkt = (nk + C::BK - 1) / C::BK;
-  // An even number of tiles; tiles past n_k arrive as zero rows, are wholly
-  // masked and add exactly nothing.
-  const int nkt2 = (nkt + 1) / 2 * 2;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)rs;
     const uint8_t* Kb = K + base_k;
@@ -307,13 +307,16 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
         }
       }
     };
-    fetch(sK0, Kb, 0);
-    fetch(sV0, Vb, 0);
-    fetch(sK1, Kb, 1);
+    // Tile t sits in slot (t + odd) mod 2, odd = (nkt - 1) mod 2, so that the
+    // pairs of the loop below end on the last tile, in slot 0.
+    const int nb = nkt - 1;
+    const bool odd = nb & 1;
+    fetch(odd ? sK1 : sK0, Kb, 0);
+    fetch(odd ? sV1 : sV0, Vb, 0);
+    if (nkt > 1) fetch(odd ? sK0 : sK1, Kb, 1);
     dma_wait();
     __syncthreads();
     f32x16 s_a[2][2], s_b[2][2];
-    scores(s_a, sK0, tile_scale(sSK, 0));
     // P's scale per query row of a tile: from the largest score of its 64 keys
     // (this lane's 32 and the other half's); alpha > 0, so sigma is increasing
     // in s. Keys at or past n_k are masked to -inf first.
@@ -341,7 +344,6 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
         pbyte[qb] = e + kE8M0One;
       }
     };
-    mask_and_scale(s_a, 0);
 
     // One tile, as a fixed step schedule (one wave per SIMD hides latency only
     // inside its own instruction stream):
@@ -351,18 +353,19 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
     // Two slots each for K and V: K runs two tiles ahead (tile t+2 goes into
     // tile t's K slot, last read by S(t) in the previous iteration), V one tile
     // ahead (tile t+1 into tile t-1's V slot). Slot X = t % 2 holds K(t) and
-    // V(t); Y = 1 - X holds K(t+1) and V(t-1).
+    // V(t); Y = 1 - X holds K(t+1) and V(t-1). The last tile's iteration
+    // (NEXT false) has no tile t+1: no DMA, no S MFMAs, only P and P V. The
+    // DMA of a tile past n_k fills its slot with zeros, which nothing reads.
     constexpr int NS = 4 * C::KS, NP = 2 * C::NB;
-    auto iteration = [&](auto x_c, int t, f32x16 (&sc)[2][2], f32x16 (&sn)[2][2]) {
-      constexpr int X = decltype(x_c)::value;
-      uint8_t* kx = X == 0 ? sK0 : sK1;
-      uint8_t* ky = X == 0 ? sK1 : sK0;
-      uint8_t* vx = X == 0 ? sV0 : sV1;
-      uint8_t* vy = X == 0 ? sV1 : sV0;
+    auto iteration = [&](auto next_c, uint8_t* kx, uint8_t* ky, uint8_t* vx, uint8_t* vy, int t,
+                         f32x16 (&sc)[2][2], f32x16 (&sn)[2][2]) __attribute__((always_inline)) {
+      constexpr bool NEXT = decltype(next_c)::value;
       dma_wait();       // this wave's DMAs of K(t+1) and V(t) have landed
       __syncthreads();  // ... everyone's have, and every wave is done with K(t) and V(t-1)
-      fetch(kx, Kb, t + 2);
-      fetch(vy, Vb, t + 1);
+      if constexpr (NEXT) {
+        fetch(kx, Kb, t + 2);
+        fetch(vy, Vb, t + 1);
+      }
       const int skb = tile_scale(sSK, t + 1), svb = tile_scale(sSV, t);
       const uint8_t* kt = ky;
       const uint8_t* vt = vx;
@@ -371,16 +374,19 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
       // Every LDS operand of the tile is requested up front: K(t+1) for the S
       // phase and V(t)^T for the P V phase, so no MFMA waits on a read.
       i32x8 a_ops[2][C::KS], b_ops[C::NB];
+      if constexpr (NEXT) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) a_ops[kb][s] = lds8_row<D>(kt, 32 * kb + l32, 4 * s + 2 * half);
+          for (int s = 0; s < C::KS; ++s) a_ops[kb][s] = lds8_row<D>(kt, 32 * kb + l32, 4 * s + 2 * half);
+      }
 #pragma unroll
       for (int db = 0; db < C::NB; ++db) b_ops[db] = lds8_vt<D>(vt, db, lane);
       static_for<0, NS>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         constexpr int kb = g / (2 * C::KS), s = (g / 2) % C::KS, qb = g % 2;
-        if constexpr (s == 0) {
+        if constexpr (!NEXT) {
+        } else if constexpr (s == 0) {
           f32x16 z;
 #pragma unroll
           for (int r = 0; r < 16; ++r) z[r] = 0.0f;
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
             p8[eq][j] = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3],
                                                         __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], 0, false), true);
         });
-        sched_step<g, 0, 1, (e1 - e0) * 9 / 2, kNoFence>();
+        sched_step<g, 0, NEXT ? 1 : 0, (e1 - e0) * 9 / 2, kNoFence>();
       });
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NP>([&](auto gc) {
@@ -406,15 +412,31 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
         oacc[qb][db] = mfma8(p8[qb], b_ops[db], oacc[qb][db], pbyte[qb], svb);
         sched_step<g, 0, 1, 8, kNoFence>();
       });
-      mask_and_scale(sn, (t + 1) * C::BK);
+      if constexpr (NEXT) mask_and_scale(sn, (t + 1) * C::BK);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    for (int t = 0; t < nkt2; t += 2) {
-      iteration(I0{}, t, s_a, s_b);
-      iteration(I1{}, t + 1, s_b, s_a);
+    using NX = std::true_type;
+    using LAST = std::false_type;
+    // Tile 0's scores; with an odd count tile 0 also runs its iteration here
+    // (slot 1) and leaves tile 1's scores in s_a. Then tiles in whole pairs up
+    // to nkt - 2, then the last tile (slot 0). A loop entered in the middle of
+    // a pair, or leftover iterations after it, made the compiler spill or
+    // shuffle registers in the loop.
+    int t = 0;
+    if (odd) {
+      scores(s_b, sK1, tile_scale(sSK, 0));
+      mask_and_scale(s_b, 0);
+      iteration(NX{}, sK1, sK0, sV1, sV0, 0, s_b, s_a);
+      t = 1;
+    } else {
+      scores(s_a, sK0, tile_scale(sSK, 0));
+      mask_and_scale(s_a, 0);
     }
-    dma_wait();  // the last iterations' DMAs (all zeros) must not outlive the kernel
+    for (; t < nb; t += 2) {
+      iteration(NX{}, sK0, sK1, sV0, sV1, t, s_a, s_b);
+      iteration(NX{}, sK1, sK0, sV1, sV0, t + 1, s_b, s_a);
+    }
+    iteration(LAST{}, sK0, sK1, sV0, sV1, nb, s_a, s_b);
+    dma_wait();  // the last DMAs (all zeros) must not outlive the kernel
   }
 
   // Register r of oacc[qb][db] holds query row 64w + 32qb + acc_row(r, half), column 32db + l%32.

@@ -69,32 +69,38 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], 
     }
 }
 
-// One key tile of the forward for one wave, written as a fixed step schedule.
-// With one wave per SIMD, latency can only be hidden inside the wave's own
-// instruction stream. The tile is two phases of NSTEP steps, 2 MFMAs each:
+// The forward of one wave, written as a fixed step schedule. With one wave per
+// SIMD, latency can only be hidden inside the wave's own instruction stream.
+// Key tile t is two phases of NSTEP steps, 2 MFMAs each:
 //   phase A: S(t, 2nd half) = K Q^T (KS steps), then O += P(t-1, 2nd half) V
 //            (2*NB steps)                          || P(t, 1st half) = sigma(S)
 //   barrier (at_barrier: the DMA of tile t+1 has landed; the next one starts)
 //   phase B: O += P(t, 1st half) V (2*NB steps), then S(t+1, 1st half)
 //            (KS steps)                            || P(t, 2nd half) = sigma(S)
-// The LDS operand of step g+3 is requested at step g, through the barrier and
-// on into the next tile's first steps. Reads that precede the barrier touch
-// only V of tile t, which landed a tile earlier; tile t+1's K is read only after
-// the barrier. Phase B puts P V first so those early reads exist. Since S of
-// phase B is finished by its last steps, phase A's sigma starts one step late.
-// ops[0..2] hold the operands of steps 0..2 on entry and of the next tile's
-// steps 0..2 on exit (2 * NSTEP is a multiple of 4, the ring depth).
-template <int D, typename AtBarrier, typename DmaChunk>
-__device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
-                                         f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                         f32x16 (&oacc)[2][FwdCfg<D>::NB], bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
-                                         bf16x8 (&ops)[4], const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0,
-                                         int l32, int half, int lane, AtBarrier&& at_barrier, DmaChunk&& dma_chunk) {
+// fwd_steps runs steps [G0, G1) of that stream for one tile. The key loop runs
+// phase B of tile t followed by phase A of tile t+1, so each loop body adds
+// exactly one key tile (t+1); the first tile's phase A (which has no tile -1)
+// and the last tile's phase B (which has no tile t+1) are written out apart
+// from the loop. The LDS operand of step g+3 is requested at step g, through
+// the barrier and on into the next phase. Reads that precede the barrier touch
+// only V of tile t, which landed a tile earlier; tile t+1's K is read only
+// after the barrier. Since S of phase B is finished by its last steps, phase
+// A's sigma starts one step late. ops[0..3] is a ring indexed by step mod 4
+// (2 * NSTEP is a multiple of 4).
+// Slots: kT, vT hold tile t; vP holds tile t-1 (phase A's P V); kN holds tile
+// t+1 (phase B's S, and the reads ahead into the next phase A).
+template <int D, int G0, int G1, typename AtBarrier, typename DmaChunk>
+__device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
+                                          f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                          f32x16 (&oacc)[2][FwdCfg<D>::NB], bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
+                                          bf16x8 (&ops)[4], const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0,
+                                          int l32, int half, int lane, AtBarrier&& at_barrier, DmaChunk&& dma_chunk) {
   using C = FwdCfg<D>;
   constexpr int KS = C::KS, NB2 = 2 * C::NB;
   constexpr int NSTEP = KS + NB2;  // steps per phase: 16 at D = 128, 8 at D = 64
   constexpr int G = 2 * NSTEP;     // steps per tile
   static_assert(G % 4 == 0 && KS >= 3 && NB2 >= 3, "ring of four operands, three steps ahead");
+  static_assert(0 <= G0 && G0 < G1 && G1 <= G, "a step range of one tile");
   // The next DMA is NDMA instructions per thread (K and V), spread one per
   // DSTRIDE steps over phase B: issued in one burst they stall the wave.
   constexpr int NDMA = 2 * kDmaChunks<D, C::BK, 256>;
@@ -121,10 +127,12 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, con
     const int h = g % G;
     return (h < KS || h >= NSTEP + NB2) ? 1 : 2;
   };
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_nxt[0][r] = s_nxt[1][r] = 0.0f;
-  static_for<0, G>([&](auto gc) {
+  static_for<G0, G1>([&](auto gc) {
     constexpr int g = decltype(gc)::value;
+    if constexpr (g == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[0][r] = s_nxt[1][r] = 0.0f;
+    }
     if constexpr (g == NSTEP) {
       pin_before_barrier(p0);
       at_barrier();
@@ -171,13 +179,18 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kT, const __bf16* vP, con
 
 // Forward. Each wave owns 64 query rows. The key loop is software-pipelined in
 // half-tiles (32 keys) so that the MFMAs of one half-tile run beside the sigma
-// of another (fwd_tile). The LDS ring holds tiles t-1, t and t+1, and there is
+// of another (fwd_steps). The LDS ring holds tiles t-1, t and t+1, and there is
 // one barrier per key tile. K and V come straight from global memory into LDS
 // by DMA, with padded key rows replaced by zeros on the way. Each ring slot is
 // its own LDS variable and the key loop is unrolled by three, so every access
 // names its slot at compile time; the compiler then sees that the reads after
 // the barrier cannot touch the slot the DMA is filling and does not wait for
 // the DMA before them.
+//
+// Exactly the key tiles below n_k are computed, each once: the prologue takes
+// tile 0's scores, each loop body one more tile, and the epilogue finishes the
+// last tile's P V. Tile t sits in slot t mod 3. tile_counts receives the
+// number of key tiles whose scores this workgroup computed.
 template <int D>
 __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -233,11 +246,8 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
 
-  const int nkt = (nk + C::BK - 1) / C::BK;
-  // The loop runs a multiple of three tiles. Tiles past n_k arrive as zeros
-  // (every DMA lane is out of range): their V rows are 0, so they add exactly
-  // nothing to O.
-  const int nkt3 = (nkt + 2) / 3 * 3;
+  const int nkt = (nk + C::BK - 1) / C::BK;  // live key tiles; no other tile is computed
+  int executed = 0;                          // key tiles whose scores this workgroup computed
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Kb = K + base_k;
@@ -248,26 +258,33 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
       dma_tile<D, C::BK, 256>(sk, Kb + off, row_bytes, nk - k0, tid);
       dma_tile<D, C::BK, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
+    // Tile t sits in slot t mod 3.
     fetch(sK0, sV0, 0);
-    fetch(sK1, sV1, 1);
-    // Slot 2's V is read by the first phase A with P = 0 (there is no tile -1).
-    // It must hold finite values then, so it starts as zeros.
-    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sV2 + c * 8) = zero_bf16x8();
+    if (nkt > 1) fetch(sK1, sV1, 1);
     dma_wait();
     __syncthreads();
 
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 p0[2][2], p1[2][2], ops[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) p1[qb][0] = p1[qb][1] = zero_bf16x8();
+    // Prologue: S(0, 1st half), then S(0, 2nd half) beside P(0, 1st half) = sigma(S).
     scores_t<D>(s_cur, sK0, 0, qf, l32, half);
+    scores_t<D>(s_nxt, sK0, 1, qf, l32, half);
 #pragma unroll
-    for (int s3 = 0; s3 < 3; ++s3) ops[s3] = lds_nat<D>(sK0, 32 + l32, 2 * s3 + half);
-    // Key tile t in slot T; slot P holds tile t-1 and slot N tile t+1.
-    auto iteration = [&](auto t_c, auto p_c, auto n_c, int t) {
+    for (int e = 0; e < 32; ++e) p0[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_dot(s_cur[e >> 4][e & 15], c1, c0);
+    interleave_mfma_valu<2 * C::KS, 10>();
+    // the operands of phase B's first three steps: V of tile 0, 1st half
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ops[(2 * C::KS + 2 * C::NB + i) % 4] = lds_tr<D>(sV0, (i & 1) * 16, (i >> 1) * 32, lane);
+    executed = 1;
+
+    // Loop body for tile t in slot T (tile t-1 in slot P, tile t+1 in slot N):
+    // phase B of tile t, then phase A of tile t+1. Phase B starts tile t+2's
+    // DMA into slot P (every wave has finished with tile t-1 at the barrier).
+    // The DMA of a tile past n_k (t + 2 = nkt) has no row in range and fills
+    // its slot with zeros, which nothing reads.
+    auto body = [&](auto t_c, auto p_c, auto n_c, int t) {
       constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      // Tile t+2's DMA into slot P, chunk i (K chunks, then V chunks). Tiles
-      // at or past n_k get no row in range and arrive as zeros.
+      constexpr int KS = C::KS, NSTEP = KS + 2 * C::NB, G = 2 * NSTEP;
       auto dma_chunk = [&](int i) {
         constexpr int NC = kDmaChunks<D, C::BK, 256>;
         const int k0 = (t + 2) * C::BK;
@@ -277,25 +294,46 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
         else
           dma_tile_chunk<D, C::BK, 256>(ring<P>(sV0, sV1, sV2), Vb + off, row_bytes, nk - k0, tid, i - NC);
       };
-      fwd_tile<D>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2), ring<N>(sK0, sK1, sK2),
-                  s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
-                  [&] {
-                    dma_wait();       // this wave's DMA of tile t+1 has landed
-                    __syncthreads();  // ... everyone's has, and every wave is done with slot P
-                  },
-                  dma_chunk);
+      auto at_barrier = [&] {
+        dma_wait();       // this wave's DMA of tile t+1 has landed
+        __syncthreads();  // ... everyone's has, and every wave is done with slot P
+      };
+      auto none = [](int) {};
+      auto no_barrier = [] {};
+      fwd_steps<D, NSTEP, G>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
+                             ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
+                             at_barrier, dma_chunk);
+      fwd_steps<D, 0, NSTEP>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
+                             ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
+                             no_barrier, none);
+      ++executed;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int t = 0; t < nkt3; t += 3) {
-      iteration(I0{}, I2{}, I1{}, t);
-      iteration(I1{}, I0{}, I2{}, t + 1);
-      iteration(I2{}, I1{}, I0{}, t + 2);
+    // Bodies for tiles 0 .. nkt-2: whole rounds of three (slots 0, 1, 2), then
+    // the one or two left over. The compiler keeps the three-body loop as free
+    // of spills as the earlier form (a loop entered or left in the middle of a
+    // round spilled up to 388 registers); the leftover bodies and the epilogue
+    // sit after it.
+    const int nb = nkt - 1, nb3 = nb / 3 * 3;
+    for (int t = 0; t < nb3; t += 3) {
+      body(I0{}, I2{}, I1{}, t);
+      body(I1{}, I0{}, I2{}, t + 1);
+      body(I2{}, I1{}, I0{}, t + 2);
     }
-    dma_wait();  // the last iterations' DMAs (all zeros) must not outlive the kernel
-    // the second half of tile nkt3 - 1 (slot 2)
-    accumulate_pv<D>(oacc, p1, sV2, 1, lane);
+    if (nb3 < nb) body(I0{}, I2{}, I1{}, nb3);
+    if (nb3 + 1 < nb) body(I1{}, I0{}, I2{}, nb3 + 1);
+    // Epilogue, the last tile (slot nb mod 3): P(1st half) V beside
+    // P(2nd half) = sigma(S), then P(2nd half) V.
+    const int last = nb - nb3;
+    const __bf16* vL = last == 0 ? sV0 : (last == 1 ? sV1 : sV2);
+    accumulate_pv<D>(oacc, p0, vL, 0, lane);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) p1[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_dot(s_nxt[e >> 4][e & 15], c1, c0);
+    interleave_mfma_valu<2 * C::NB * 2, 10>();
+    accumulate_pv<D>(oacc, p1, vL, 1, lane);
+    dma_wait();  // the last body's DMA (all zeros) must not outlive the kernel
   }
 
   // Epilogue. Register r of oacc[qb][db] holds query row 64w + 32qb + acc_row(r, half), column 32db + l%32.
@@ -308,7 +346,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
         const int row = q0 + 64 * w + 32 * qb + acc_row(r, half);
         if (row < rows) Ob[(size_t)row * rs + db * 32 + l32] = (__bf16)(row < nq ? oacc[qb][db][r] : 0.0f);
       }
-  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = nkt;
+  if (tile_counts != nullptr && tid == 0) tile_counts[((size_t)z * H + h) * n_qt + m] = executed;
 }
 
 // ---------------------------------------------------------------------------------------------
