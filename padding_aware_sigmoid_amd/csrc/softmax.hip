@@ -61,10 +61,18 @@ __device__ __forceinline__ void softmax_block_max(const f32x16& s, float& mx) {
   mx = fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
 }
 
-template <int D>
+// Lazy rescale before a block's exponentials. The reference maximum m is an
+// integer (log2 units), so the rescale factor f = 2^(m_old - m_new) is a power
+// of two and scales O^T, the row sum and the pending P block exactly. The
+// pending block (HAS_PENDING) is the previous block's P, already added into
+// lsum but not yet into O^T (its P V MFMAs run after this point in the
+// schedule): it is brought to the new m with the rest. Without that, a block
+// whose maximum rises more than kRescaleLog2 above m would add the previous
+// block's P V at the old scale.
+template <int D, bool HAS_PENDING>
 __device__ __forceinline__ void softmax_rescale_if_needed(f32x16 (&s)[2], f32x16 (&oT)[2][SmCfg<D>::NB],
-                                                          float (&m)[2], float (&lsum)[2], float c1, int key0,
-                                                          int nk, int half) {
+                                                          float (&m)[2], float (&lsum)[2], bf16x8 (&pending)[2][2],
+                                                          float c1, int key0, int nk, int half) {
   // mask keys >= n_k. Register r of lane l holds key key0 + (r/4)*8 + 4*half + r%4.
   if (key0 + 32 > nk) {
     const int lim = nk - key0 - 4 * half;
@@ -87,13 +95,19 @@ __device__ __forceinline__ void softmax_rescale_if_needed(f32x16 (&s)[2], f32x16
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mp = fmaxf(mc[qb], __shfl_xor(mc[qb], 32));
-      const float mn = fmaxf(m[qb], mp);
-      const float f = __builtin_amdgcn_exp2f(m[qb] - mn);  // 0 when m was -inf
+      const float mn = fmaxf(m[qb], __builtin_ceilf(mp));
+      const float f = __builtin_amdgcn_exp2f(m[qb] - mn);  // 0 when m was -inf; else 2^-k, k a whole number
       lsum[qb] *= f;
 #pragma unroll
       for (int db = 0; db < SmCfg<D>::NB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oT[qb][db][r] *= f;
+      if constexpr (HAS_PENDING) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pending[qb][ks][j] = (__bf16)((float)pending[qb][ks][j] * f);
+      }
       m[qb] = mn;
     }
   }
@@ -111,25 +125,29 @@ __device__ __forceinline__ void softmax_elem(bf16x8 (&p)[2][2], float (&lsum)[2]
   }
 }
 
-// One key tile for one wave, as the sigmoid forward's tile schedule:
+// The forward of one wave, in the sigmoid forward's step schedule. Key tile t
+// is two phases:
 //   phase A: S(t, 2nd half) (KS steps), then O^T += V(t-1, 2nd half)^T P (2*NB steps)
 //            || P(t, 1st half) = softmax part of S(t, 1st half)
 //   barrier
 //   phase B: O^T += V(t, 1st half)^T P (2*NB steps), then S(t+1, 1st half) (KS steps)
 //            || P(t, 2nd half) = softmax part of S(t, 2nd half)
-// Each phase first takes its block's maximum (and rescales if needed); the
-// exponentials are then spread over the steps.
-template <int D, typename AtBarrier, typename DmaChunk>
-__device__ __forceinline__ void sm_tile(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
-                                        f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], f32x16 (&oT)[2][SmCfg<D>::NB],
-                                        bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2], float (&m)[2], float (&lsum)[2],
-                                        bf16x8 (&ops)[4], const bf16x8 (&qf)[2][SmCfg<D>::KS], float c1, int key_t,
-                                        int nk, int l32, int half, int lane, AtBarrier&& at_barrier,
-                                        DmaChunk&& dma_chunk) {
+// Each phase first takes its block's maximum (and rescales if needed, the
+// other phase's pending P included); the exponentials are then spread over
+// the steps. sm_steps runs steps [G0, G1) of one tile's stream; the key loop
+// runs phase B of tile t, then phase A of tile t+1. key_t is tile t's first key.
+template <int D, int G0, int G1, typename AtBarrier, typename DmaChunk>
+__device__ __forceinline__ void sm_steps(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
+                                         f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], f32x16 (&oT)[2][SmCfg<D>::NB],
+                                         bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2], float (&m)[2], float (&lsum)[2],
+                                         bf16x8 (&ops)[4], const bf16x8 (&qf)[2][SmCfg<D>::KS], float c1, int key_t,
+                                         int nk, int l32, int half, int lane, AtBarrier&& at_barrier,
+                                         DmaChunk&& dma_chunk) {
   using C = SmCfg<D>;
   constexpr int KS = C::KS, NB2 = 2 * C::NB;
   constexpr int NSTEP = KS + NB2;
   constexpr int G = 2 * NSTEP;
+  static_assert(0 <= G0 && G0 < G1 && G1 <= G, "a step range of one tile");
   constexpr int NDMA = 2 * kDmaChunks<D, C::BK, 256>;
   constexpr int DSTRIDE = NSTEP / NDMA > 0 ? NSTEP / NDMA : 1;
   auto read = [&](auto gc) -> bf16x8 {
@@ -152,17 +170,20 @@ __device__ __forceinline__ void sm_tile(const __bf16* kT, const __bf16* vP, cons
     const int h = g % G;
     return (h < KS || h >= NSTEP + NB2) ? 1 : 2;
   };
-  // phase A's block: S(t, 1st half), keys key_t .. key_t + 31
-  softmax_rescale_if_needed<D>(s_cur, oT, m, lsum, c1, key_t, nk, half);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_nxt[0][r] = s_nxt[1][r] = 0.0f;
-  static_for<0, G>([&](auto gc) {
+  static_for<G0, G1>([&](auto gc) {
     constexpr int g = decltype(gc)::value;
+    if constexpr (g == 0) {
+      // phase A's block: S(t, 1st half), keys key_t .. key_t + 31; p1 (tile
+      // t-1, 2nd half) is still to be added into O^T
+      softmax_rescale_if_needed<D, true>(s_cur, oT, m, lsum, p1, c1, key_t, nk, half);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[0][r] = s_nxt[1][r] = 0.0f;
+    }
     if constexpr (g == NSTEP) {
       pin_before_barrier(p0);
       at_barrier();
-      // phase B's block: S(t, 2nd half), keys key_t + 32 .. key_t + 63
-      softmax_rescale_if_needed<D>(s_nxt, oT, m, lsum, c1, key_t + 32, nk, half);
+      // phase B's block: S(t, 2nd half), keys key_t + 32 .. key_t + 63; p0 is pending
+      softmax_rescale_if_needed<D, true>(s_nxt, oT, m, lsum, p0, c1, key_t + 32, nk, half);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_cur[0][r] = s_cur[1][r] = 0.0f;
     }
@@ -267,8 +288,11 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(cons
       for (int r = 0; r < 16; ++r) oT[qb][db][r] = 0.0f;
   float m[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.0f, 0.0f};
 
+  // Exactly the key tiles below n_k are computed, each once, as in the
+  // sigmoid forward: tile 0's scores in the prologue, one more tile per loop
+  // body (phase B of tile t, phase A of tile t+1), the last tile's P V in the
+  // epilogue. Tile t sits in slot t mod 3.
   const int nkt = (nk + C::BK - 1) / C::BK;
-  const int nkt3 = (nkt + 2) / 3 * 3;
   if (nkt > 0) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const __bf16* Kb = K + base_k;
@@ -280,18 +304,15 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(cons
       dma_tile<D, C::BK, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
     fetch(sK0, sV0, 0);
-    fetch(sK1, sV1, 1);
-    for (int c = tid; c < C::TILE / 8; c += 256) *(bf16x8*)(sV2 + c * 8) = zero_bf16x8();
+    if (nkt > 1) fetch(sK1, sV1, 1);
     dma_wait();
     __syncthreads();
 
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 p0[2][2], p1[2][2], ops[4];
+    // Prologue: S(0, 1st half) and S(0, 2nd half) = K Q^T, then P(0, 1st half).
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) p1[qb][0] = p1[qb][1] = zero_bf16x8();
-    // S(0, 1st half) = K Q^T
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s_cur[0][r] = s_cur[1][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) s_cur[0][r] = s_cur[1][r] = s_nxt[0][r] = s_nxt[1][r] = 0.0f;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const bf16x8 a = lds_nat<D>(sK0, l32, 2 * s + half);
@@ -299,9 +320,24 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(cons
       s_cur[1] = mfma32(a, qf[1][s], s_cur[1]);
     }
 #pragma unroll
-    for (int s3 = 0; s3 < 3; ++s3) ops[s3] = lds_nat<D>(sK0, 32 + l32, 2 * s3 + half);
-    auto iteration = [&](auto t_c, auto p_c, auto n_c, int t) {
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 a = lds_nat<D>(sK0, 32 + l32, 2 * s + half);
+      s_nxt[0] = mfma32(a, qf[0][s], s_nxt[0]);
+      s_nxt[1] = mfma32(a, qf[1][s], s_nxt[1]);
+    }
+    softmax_rescale_if_needed<D, false>(s_cur, oT, m, lsum, p1, c1, 0, nk, half);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) softmax_elem(p0, lsum, s_cur, m, c1, e);
+    // the operands of phase B's first three steps: V of tile 0, 1st half
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ops[(2 * C::KS + 2 * C::NB + i) % 4] = lds_tr<D>(sV0, (i & 1) * 16, (i >> 1) * 32, lane);
+
+    // Body for tile t in slot T (tile t-1 in slot P, which receives tile t+2;
+    // tile t+1 in slot N). The DMA of a tile past n_k fills its slot with
+    // zeros, which nothing reads.
+    auto body = [&](auto t_c, auto p_c, auto n_c, int t) __attribute__((always_inline)) {
       constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
+      constexpr int NSTEP = C::KS + 2 * C::NB, G = 2 * NSTEP;
       auto dma_chunk = [&](int i) {
         constexpr int NC = kDmaChunks<D, C::BK, 256>;
         const int k0 = (t + 2) * C::BK;
@@ -311,24 +347,41 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(cons
         else
           dma_tile_chunk<D, C::BK, 256>(ring<P>(sV0, sV1, sV2), Vb + off, row_bytes, nk - k0, tid, i - NC);
       };
-      sm_tile<D>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2), ring<N>(sK0, sK1, sK2),
-                 s_cur, s_nxt, oT, p0, p1, m, lsum, ops, qf, c1, t * C::BK, nk, l32, half, lane,
-                 [&] {
-                   dma_wait();
-                   __syncthreads();
-                 },
-                 dma_chunk);
+      auto at_barrier = [&] {
+        dma_wait();
+        __syncthreads();
+      };
+      sm_steps<D, NSTEP, G>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
+                            ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oT, p0, p1, m, lsum, ops, qf, c1, t * C::BK, nk,
+                            l32, half, lane, at_barrier, dma_chunk);
+      sm_steps<D, 0, NSTEP>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
+                            ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oT, p0, p1, m, lsum, ops, qf, c1, (t + 1) * C::BK,
+                            nk, l32, half, lane, [] {}, [](int) {});
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int t = 0; t < nkt3; t += 3) {
-      iteration(I0{}, I2{}, I1{}, t);
-      iteration(I1{}, I0{}, I2{}, t + 1);
-      iteration(I2{}, I1{}, I0{}, t + 2);
+    // Whole rounds of three bodies, then the one or two left over (a loop
+    // entered or left in the middle of a round spills heavily).
+    const int nb = nkt - 1, nb3 = nb / 3 * 3;
+    for (int t = 0; t < nb3; t += 3) {
+      body(I0{}, I2{}, I1{}, t);
+      body(I1{}, I0{}, I2{}, t + 1);
+      body(I2{}, I1{}, I0{}, t + 2);
     }
-    dma_wait();
-    sm_accumulate_pv<D>(oT, p1, sV2, 1, lane);
+    if (nb3 < nb) body(I0{}, I2{}, I1{}, nb3);
+    if (nb3 + 1 < nb) body(I1{}, I0{}, I2{}, nb3 + 1);
+    // Epilogue, the last tile (slot nb mod 3): phase B without the next
+    // tile's scores, then the P V of its second half.
+    const int last = nb - nb3;
+    const __bf16* vL = last == 0 ? sV0 : (last == 1 ? sV1 : sV2);
+    softmax_rescale_if_needed<D, true>(s_nxt, oT, m, lsum, p0, c1, nb * C::BK + 32, nk, half);
+    sm_accumulate_pv<D>(oT, p0, vL, 0, lane);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) softmax_elem(p1, lsum, s_nxt, m, c1, e);
+    interleave_mfma_valu<2 * C::NB * 2, 8>();
+    sm_accumulate_pv<D>(oT, p1, vL, 1, lane);
+    dma_wait();  // the last body's DMA (all zeros) must not outlive the kernel
   }
 
   // Epilogue: combine the two half-lanes' row sums, normalise, store O and LSE.

@@ -231,3 +231,51 @@ def test_softmax_fullsize_sampled(name):
     assert lse_d <= LSE_TOL["bf16"], f"{name}: softmax LSE err {lse_d:.3e}"
     del dq_, dk_, dv_, ddo, o, gq, gk, gv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_softmax_scores_that_keep_growing(D):
+    """Scores rise along the keys, by about 7.7 per 32-key block (11 in log2
+    units), so a block's maximum usually lies far above the forward's running
+    reference: such blocks force its lazy rescale while the previous block's
+    P still waits for its P V MFMAs, and that P must be rescaled with O and
+    the row sum. One sample is cut at n_k = 200 so the masked tail takes part.
+    O and LSE are held to the usual bounds. The gradients are held to 2^-7 of
+    the sum of their terms' absolute values (4 bf16 unit roundoffs, the bf16
+    counterpart of the fp32 bound above): with keys this close to one common
+    direction, dS K cancels almost completely (the rows of dS sum to 0), so a
+    bound relative to the result would measure that cancellation, not the
+    kernels. The backward recomputes P from LSE and has no running maximum."""
+    import padding_aware_sigmoid_amd as sa
+
+    Z, L, H = 2, 256, 1
+    nq, nk = [256, 256], [256, 200]
+    note(f"softmax growing scores D={D}")
+    g = torch.Generator().manual_seed(71)
+    q = torch.full((Z, L, H, D), 0.5)
+    # key j: components t_j + 0.1 N(0, 1), t_j = 0.24 j / D, so q.k_j is about 0.12 j
+    t = 0.24 * torch.arange(L, dtype=torch.float32) / D
+    k = t[None, :, None, None] + 0.1 * torch.randn(Z, L, H, D, generator=g)
+    v = torch.randn(Z, L, H, D, generator=g)
+    do = torch.randn(Z, L, H, D, generator=g)
+    q, k, v, do = (x.to(torch.bfloat16) for x in (q, k, v, do))
+    dq_, dk_, dv_, ddo, dnq, dnk = device_inputs(q, k, v, do, nq, nk)
+    alpha = 2.0
+    Q, K, V, DO = (f64(x) for x in (q, k, v, do))
+    # the blocks whose maximum rises past the rescale threshold (8 in log2 units)
+    blk = (alpha * (Q[0, 0, 0] @ K[0, :, 0].T) * np.log2(np.e)).reshape(-1, 32).max(axis=1)
+    rises = int(np.sum(np.diff(np.maximum.accumulate(blk)) > 8.0))
+    assert rises >= 4, f"only {rises} blocks rise past the rescale threshold"
+    o, lse = sa.sigattn_softmax_fwd(dq_, dk_, dv_, dnq, dnk, alpha)
+    gq, gk, gv = sa.sigattn_softmax_bwd(dq_, dk_, dv_, o, ddo, lse, dnq, dnk, alpha)
+    torch.cuda.synchronize()
+    ro, rlse = SM.forward(Q, K, V, nq, nk, alpha)
+    rq, rk, rv = SM.backward(Q, K, V, DO, nq, nk, alpha)
+    e = rel_err(host(o), ro)
+    assert e <= TOL["bf16"], f"O: rel err {e:.3e}"
+    e = _lse_err(lse.cpu().numpy().astype(np.float64), rlse.transpose(0, 2, 1), "bf16")
+    assert e <= LSE_TOL["bf16"], f"LSE err {e:.3e}"
+    scales = _abs_term_scales(Q, K, V, DO, nq, nk, alpha)
+    for name, got, ref in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
+        d = float(np.max(np.abs(host(got) - ref)))
+        assert d <= 2.0**-7 * scales[name], f"{name}: max abs err {d:.3e} > {2.0**-7 * scales[name]:.3e}"
