@@ -249,6 +249,28 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sigattn_softmax_bwd without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The call allocates nothing. The row statistics
+ * {LSE log2 e, Dvec} live instead in a fixed buffer inside the library of
+ * SIGATTN_NOALLOC_ROWS float pairs (16 MiB), one per GPU, which each GPU the
+ * library runs on holds until the process ends. The first call on a device
+ * looks up that device's buffer address (hipGetSymbolAddress), once.
+ * Limit: Z * L * H <= SIGATTN_NOALLOC_ROWS (both layouts: a packed batch within
+ * its contract has at most Z * L query rows), else SIGATTN_EINVAL.
+ * Every call on one GPU uses that GPU's buffer, and the buffer keeps the last
+ * call's contents (each call writes every entry it reads before reading it):
+ * calls that overlap on one GPU, on two streams or from two threads, race
+ * and give wrong results. Arguments, errors and results are those of
+ * sigattn_softmax_bwd, bit for bit.
+ */
+#define SIGATTN_NOALLOC_ROWS (1 << 21)
+int sigattn_softmax_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                const int32_t* seq_q, const int32_t* seq_k, sigattn_layout layout,
+                                int Z, int L, int H, int D, float alpha, sigattn_dtype dtype, void* stream);
+
+/*
  * FP8 forward (OCP E4M3 operands on the gfx950 FP8 MFMA), the FP8 direction
  * the pages leave as future work (rainbus.top summary of arXiv:2604.27124,
  * "未来方向"; paperlayer.ai summary, section 5), on the sigmoid forward above.

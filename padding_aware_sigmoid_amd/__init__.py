@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     KERNEL_FWD,
     LAYOUT_PACKED,
     LAYOUT_PADDED,
+    NOALLOC_ROWS,
     SigattnError,
     lib_path,
     load,
@@ -35,6 +36,7 @@ from .ops import (  # noqa: F401
     sigattn_fwd_varlen,
     sigattn_quantize_fp8,
     sigattn_softmax_bwd,
+    sigattn_softmax_bwd_noalloc,
     sigattn_softmax_fwd,
     sigattn_tile_config,
     sigmoid_attention,

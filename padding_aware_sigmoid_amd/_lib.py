@@ -18,6 +18,7 @@ BF16, FP32 = 0, 1
 KERNEL_FWD, KERNEL_DQ, KERNEL_DKDV = 0, 1, 2
 LAYOUT_PADDED, LAYOUT_PACKED = 0, 1
 BIAS_CONSTANT, BIAS_NEG_LOG_NK = 0, 1
+NOALLOC_ROWS = 1 << 21  # SIGATTN_NOALLOC_ROWS
 
 EXPORTED_SYMBOLS = (
     "sigattn_fwd",
@@ -31,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "sigattn_softmax_fwd",
     "sigattn_softmax_bwd",
     "sigattn_softmax_bwd_workspace_size",
+    "sigattn_softmax_bwd_noalloc",
     "sigattn_quantize_fp8",
     "sigattn_fwd_fp8",
     "sigattn_tile_config",
@@ -79,6 +81,9 @@ def load():
     lib.sigattn_softmax_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                         i32, vp, sz, vp]
     lib.sigattn_softmax_bwd.restype = i32
+    lib.sigattn_softmax_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                f32, i32, vp]
+    lib.sigattn_softmax_bwd_noalloc.restype = i32
     lib.sigattn_softmax_bwd_workspace_size.argtypes = [ctypes.c_longlong, i32]
     lib.sigattn_softmax_bwd_workspace_size.restype = sz
     lib.sigattn_quantize_fp8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]

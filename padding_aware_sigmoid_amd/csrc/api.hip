@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sigattn.h"
 #include "common.hpp"
@@ -308,30 +309,16 @@ size_t sigattn_softmax_bwd_workspace_size(long long rows_q, int H) {
   return rows_q > 0 && H > 0 ? (size_t)rows_q * (size_t)H * 8 : 0;
 }
 
-int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv, const int32_t* seq_q, const int32_t* seq_k,
-                        sigattn_layout layout, int Z, int L, int H, int D, float alpha, sigattn_dtype dtype,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
-  int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
-  if (rc != 0) return rc;
-  if (!(alpha > 0.0f)) return fail(SIGATTN_EINVAL, "softmax needs alpha > 0%s");
-  rc = check_common(Z, L, H, D, alpha, 0.0f, dtype, seq_q, seq_k);
-  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
-  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
-      (rc = check_tensor(o, "o")) || (rc = check_tensor(dout, "dout")) || (rc = check_tensor(lse, "lse")) ||
-      (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")) ||
-      (rc = check_tensor(workspace, "workspace")))
-    return rc;
-  // The padded layout has Z * L query rows. The packed layout's row count sits
-  // in device memory (the last offset): there only the one-row-per-sample floor
-  // is checked here, and the caller sizes the buffer for all of its rows.
-  const size_t rows = layout == SIGATTN_LAYOUT_PADDED ? (size_t)Z * L : (size_t)Z;
-  if (workspace_bytes < rows * (size_t)H * 8)
-    return fail(SIGATTN_EWORKSPACE, "workspace smaller than query rows * H * 8 bytes%s");
-  const sigattn::SeqLayout sl{seq_q, seq_k, L, layout, 0};
+}  // extern "C"
+
+namespace {
+
+// The row statistics pass, then the fused dK/dV and the dQ kernels (bf16), or
+// the fp32 validation kernels, with the row statistics in `workspace`.
+int run_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, const sigattn::SeqLayout& sl, int Z, int H, int D, float alpha,
+                    int dtype, void* workspace, hipStream_t st) {
   const float c1 = alpha * kLog2e;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int bf = dtype == SIGATTN_BF16;
   hipError_t e = (D == 64) ? sigattn::launch_sm_rowstats<64>(bf, o, dout, lse, workspace, sl, Z, H, alpha, st)
                            : sigattn::launch_sm_rowstats<128>(bf, o, dout, lse, workspace, sl, Z, H, alpha, st);
@@ -350,6 +337,99 @@ int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void*
                   : sigattn::launch_sm_bwd_fp32<128>(q, k, v, dout, workspace, dq, dk, dv, sl, Z, H, alpha, c1, st);
   }
   return hip_status(e);
+}
+
+// Checks shared by both softmax backward entry points. Returns 0 to proceed,
+// 1 for an empty batch, or a negative status.
+int check_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, const int32_t* seq_q, const int32_t* seq_k, int layout, int Z,
+                      int L, int H, int D, float alpha, int dtype) {
+  int rc = check_modes(layout, SIGATTN_BIAS_CONSTANT);
+  if (rc != 0) return rc;
+  if (!(alpha > 0.0f)) return fail(SIGATTN_EINVAL, "softmax needs alpha > 0%s");
+  rc = check_common(Z, L, H, D, alpha, 0.0f, dtype, seq_q, seq_k);
+  if (rc != 0) return rc;
+  if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
+      (rc = check_tensor(o, "o")) || (rc = check_tensor(dout, "dout")) || (rc = check_tensor(lse, "lse")) ||
+      (rc = check_tensor(dq, "dq")) || (rc = check_tensor(dk, "dk")) || (rc = check_tensor(dv, "dv")))
+    return rc;
+  return 0;
+}
+
+// The device-resident row statistics of sigattn_softmax_bwd_noalloc: one
+// array per GPU, of fixed size, for the life of the process. Host code never
+// uses the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and kept in scratch_ptr.
+constexpr size_t kScratchPairs = (size_t)SIGATTN_NOALLOC_ROWS;
+static_assert(kScratchPairs * sizeof(float2) == ((size_t)16 << 20), "16 MiB of row statistics per GPU");
+static __device__ __align__(256) float2 scratch[kScratchPairs];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The address of `scratch` on the device that runs `st` (the current device
+// for the null stream).
+int scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(SIGATTN_EINVAL, "device index out of the supported range%s");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_status(e);
+    if (back != hipSuccess) return hip_status(back);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SIGATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sigattn_softmax_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, const int32_t* seq_q, const int32_t* seq_k,
+                        sigattn_layout layout, int Z, int L, int H, int D, float alpha, sigattn_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_softmax_bwd(q, k, v, o, dout, lse, dq, dk, dv, seq_q, seq_k, layout, Z, L, H, D, alpha, dtype);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  if ((rc = check_tensor(workspace, "workspace"))) return rc;
+  // The padded layout has Z * L query rows. The packed layout's row count sits
+  // in device memory (the last offset): there only the one-row-per-sample floor
+  // is checked here, and the caller sizes the buffer for all of its rows.
+  const size_t rows = layout == SIGATTN_LAYOUT_PADDED ? (size_t)Z * L : (size_t)Z;
+  if (workspace_bytes < rows * (size_t)H * 8)
+    return fail(SIGATTN_EWORKSPACE, "workspace smaller than query rows * H * 8 bytes%s");
+  return run_softmax_bwd(q, k, v, o, dout, lse, dq, dk, dv, {seq_q, seq_k, L, layout, 0}, Z, H, D, alpha, dtype,
+                         workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sigattn_softmax_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, const int32_t* seq_q,
+                                const int32_t* seq_k, sigattn_layout layout, int Z, int L, int H, int D, float alpha,
+                                sigattn_dtype dtype, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_softmax_bwd(q, k, v, o, dout, lse, dq, dk, dv, seq_q, seq_k, layout, Z, L, H, D, alpha, dtype);
+  if (rc != 0) return rc > 0 ? SIGATTN_OK : rc;
+  // Both layouts hold at most Z * L query rows (a packed batch within its
+  // contract: no sample longer than L).
+  if ((unsigned long long)Z * (unsigned long long)L * (unsigned long long)H > kScratchPairs)
+    return fail(SIGATTN_EINVAL, "Z * L * H exceeds the fixed row-statistics buffer (SIGATTN_NOALLOC_ROWS)%s");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = scratch_address(st, &ws)) != SIGATTN_OK) return rc;
+  return run_softmax_bwd(q, k, v, o, dout, lse, dq, dk, dv, {seq_q, seq_k, L, layout, 0}, Z, H, D, alpha, dtype, ws,
+                         st);
 }
 
 int sigattn_quantize_fp8(const void* x, void* x8, uint8_t* scales, const int32_t* seq, sigattn_layout layout,

@@ -441,6 +441,30 @@ def sigattn_softmax_bwd(q, k, v, o, dout, lse, seq_q, seq_k, alpha=None, dq=None
     return dq, dk, dv
 
 
+def sigattn_softmax_bwd_noalloc(q, k, v, o, dout, lse, seq_q, seq_k, alpha=None, dq=None, dk=None, dv=None,
+                                max_len=None):
+    """sigattn_softmax_bwd with the library's fixed device buffer for the row
+    statistics instead of a workspace (wraps sigattn_softmax_bwd_noalloc): the
+    C call allocates nothing. Z * L * H must not exceed NOALLOC_ROWS, and calls
+    that overlap on one GPU race. Pass dq, dk and dv to allocate nothing here
+    either."""
+    layout, Z, L, sq, sk = _softmax_layout(q, k, seq_q, seq_k, max_len, {"o": o, "dout": dout}, {"v": v})
+    H, D = q.shape[-2], q.shape[-1]
+    alpha = default_alpha(D) if alpha is None else float(alpha)
+    _check_lse(lse, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+            raise ValueError(f"{name} must match {'q' if ref is q else 'k'} in shape, dtype and device")
+    _lib.check(_lib.load().sigattn_softmax_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                       dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                                       dv.data_ptr(), sq.data_ptr(), sk.data_ptr(), layout, Z, L, H, D,
+                                                       alpha, _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
+
+
 class SoftmaxAttention(torch.autograd.Function):
     """Autograd wrapper of the softmax path. The forward saves its inputs, O and
     LSE; the backward recomputes P from them."""
