@@ -58,6 +58,9 @@ def parse():
                     help="workload of the FP8 forward sub-object ('' to skip)")
     ap.add_argument("--softmax-workload", default="nopad16k",
                     help="workload of the softmax fwd+bwd sub-object ('' to skip)")
+    ap.add_argument("--configs", default="tiny,nopad16k,pad25_16k,cellbatch8k,stress8k@1,stress8k@4,stress8k@16",
+                    help="workloads (name or name@qk_scale) whose per-pass TFLOP/s the line reports under 'configs' "
+                         "('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many bytes twice (a plain device copy of "
@@ -65,14 +68,14 @@ def parse():
     return ap.parse_args()
 
 
-def run_gpu(name, steps, warmup, seed=0):
+def run_gpu(name, steps, warmup, seed=0, qk_scale=None):
     import torch
 
     import padding_aware_sigmoid_amd as sa
     import workloads
     from padding_aware_sigmoid_amd import accounting
 
-    inp = workloads.make_inputs(name, seed=seed)
+    inp = workloads.make_inputs(name, seed=seed, qk_scale=qk_scale)
     w = inp["workload"]
     dev = torch.device("cuda:0")
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
@@ -121,8 +124,11 @@ def run_gpu(name, steps, warmup, seed=0):
     ms_step = elapsed / steps * 1e3
     res = {
         "workload": w,
+        "qk_scale": inp["qk_scale"],
         "lengths": inp["seqlens_q"].tolist(),
         "ms_per_step": ms_step,
+        "fwd_ms": t_fwd,
+        "bwd_ms": t_bwd,
         "tflops_valid": fl["total_valid"] / (ms_step * 1e-3) / 1e12,
         "tflops_padded": fl["total_padded"] / (ms_step * 1e-3) / 1e12,
         "fwd_tflops_valid": fl["fwd_valid"] / (t_fwd * 1e-3) / 1e12,
@@ -292,33 +298,102 @@ def run_softmax(name, steps, warmup, seed=0):
     return out
 
 
-def cpu_baseline(name, heads=2):
-    """The oracle, as it stands, on `heads` (z, h) heads of the workload at full length: fwd + bwd."""
+def host_description():
+    """Who ran the CPU baseline: core counts, CPU model, BLAS threads."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["cores_usable"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["cores_usable"] = os.cpu_count()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        pools = threadpool_info()
+        info["blas"] = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in pools]
+        info["blas_threads"] = max([i.get("num_threads", 1) for i in pools] or [1])
+    except Exception:  # noqa: BLE001
+        info["blas_threads"] = None
+    return info
+
+
+# The CPU baseline's samples: (config key, workload, qk_scale, sample z,
+# heads). One whole (z, h) head each, at the sample's true length, fwd + bwd:
+# the oracle's cost depends on n_q * n_k * D only, so one head stands for the
+# others of its sample, and its TFLOP/s for the config. To bound the run (the
+# oracle is slow), the 25%-padding config takes its shortest sample and the
+# cell-batch and stress configs their median one; the score scale of the
+# stress config does not change the oracle's work, so s = 1 stands for all.
+CPU_SAMPLES = (("tiny", "tiny", None, None, None), ("nopad16k", "nopad16k", None, 0, 1),
+               ("pad25_16k", "pad25_16k", None, "shortest", 1), ("cellbatch8k", "cellbatch8k", None, "median", 1),
+               ("stress8k", "stress8k", 1.0, "median", 1))
+
+
+def cpu_baseline(main_name):
+    """The oracle, as it stands, fwd + bwd on one whole head of every config
+    (tiny: the whole batch), in float64 (the oracle) and in float32 (its
+    timing mode), on the host cores. value: float64 on the main workload."""
     import numpy as np
 
     import oracle
     import workloads
 
-    try:
-        from threadpoolctl import threadpool_info
+    per = {}
+    for key, name, scale, zsel, heads in CPU_SAMPLES:
+        w = workloads.WORKLOADS[name]
+        n_all = workloads.lengths(w, 0)
+        if zsel is None:  # the whole batch
+            Zs, Hs, n = w.Z, w.H, n_all
+            q, k, v, do = workloads.make_tensors(w.Z, w.L, w.H, w.D, w.dtype, seed=0)
+        else:
+            order = np.argsort(n_all, kind="stable")
+            z = int(order[len(n_all) // 2] if zsel == "median" else (order[0] if zsel == "shortest" else zsel))
+            Zs, Hs, n = 1, heads, n_all[z:z + 1]
+            q, k, v, do = workloads.make_tensors(1, w.L, heads, w.D, w.dtype, seed=0, qk_scale=scale or 1.0)
+        Q, K, V, DO = (t.float().numpy() for t in (q, k, v, do))
+        flop = 3.5 * 4.0 * w.D * float(np.sum(n.astype(np.int64) ** 2)) * Hs
+        rec = {"workload": name, "sample": "batch" if zsel is None else f"z={z}", "Z": Zs, "H": Hs, "D": w.D,
+               "lengths": n.tolist()}
+        for dt in oracle.sigmoid_attention.TIMING_DTYPES:
+            t0 = time.perf_counter()
+            oracle.forward(Q, K, V, n, n, w.alpha, w.bias, dtype=dt)
+            oracle.backward(Q, K, V, DO, n, n, w.alpha, w.bias, dtype=dt)
+            dt_s = time.perf_counter() - t0
+            rec[np.dtype(dt).name] = {"seconds": round(dt_s, 3), "tflops": flop / dt_s / 1e12}
+        per[key] = rec
+    host = host_description()
+    main = per[main_name]
+    return {"value": main["float64"]["tflops"], "unit": "TFLOP/s", "cores": host.get("blas_threads") or host["nproc"],
+            "kind": "oracle",
+            "sample": f"one whole (z,h) head of {main_name} (n={main['lengths'][0]}, D={main['D']}), fwd+bwd, the "
+                      f"oracle in NumPy float64, {main['float64']['seconds']:.1f} s; FLOPs counted as for the GPU "
+                      f"(3.5 x 4*D*n^2 per head). Every config in float64 and float32 under 'configs'.",
+            "host": host, "configs": per}
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    w = workloads.WORKLOADS[name]
-    n = int(workloads.lengths(w, 0)[0])
-    q, k, v, do = workloads.make_tensors(1, w.L, heads, w.D, w.dtype, seed=0)
-    Q, K, V, DO = (t.float().numpy() for t in (q, k, v, do))
-    nn = np.array([n])
-    t0 = time.perf_counter()
-    oracle.forward(Q, K, V, nn, nn, w.alpha, w.bias)
-    oracle.backward(Q, K, V, DO, nn, nn, w.alpha, w.bias)
-    dt = time.perf_counter() - t0
-    flop = 3.5 * 4.0 * w.D * n * n * heads
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} (z,h) heads of {name} at full length (L={w.L}, n={n}, D={w.D}), fwd+bwd in NumPy "
-                      f"float64, {dt:.1f} s; FLOPs counted as for the GPU (3.5 x 4*D*n^2 per head)",
-            "seconds": round(dt, 2)}
+
+def config_record(res):
+    """Per-pass TFLOP/s of one workload's run, on valid and on padded FLOPs."""
+    w, fl = res["workload"], res["flops"]
+    tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)  # noqa: E731
+    return {"workload": w.name, "Z": w.Z, "H": w.H, "L": w.L, "D": w.D, "dtype": w.dtype,
+            "qk_scale": res["qk_scale"], "lengths": res["lengths"],
+            "fwd_ms": round(res["fwd_ms"], 4), "bwd_ms": round(res["bwd_ms"], 4),
+            "ms_per_step": round(res["ms_per_step"], 4),
+            "fwd_tflops_valid": tf(fl["fwd_valid"], res["fwd_ms"]),
+            "bwd_tflops_valid": tf(fl["bwd_valid"], res["bwd_ms"]),
+            "tflops_valid": tf(fl["total_valid"], res["ms_per_step"]),
+            "fwd_tflops_padded": tf(fl["fwd_padded"], res["fwd_ms"]),
+            "bwd_tflops_padded": tf(fl["bwd_padded"], res["bwd_ms"]),
+            "tflops_padded": tf(fl["total_padded"], res["ms_per_step"]),
+            "frac_of_bf16_peak_valid": round(fl["total_valid"] / (res["ms_per_step"] * 1e-3) / 1e12
+                                             / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms": {k: round(v["ms"], 4) for k, v in res["kernels"].items()}}
 
 
 def traffic_for(kernel_name: str, workload: str):
@@ -354,6 +429,18 @@ def main():
     sa.load()
     main_res = run_gpu(args.workload, args.steps, args.warmup)
     pad_res = run_gpu(args.pad_workload, args.steps, args.warmup) if args.pad_workload not in ('', 'none') else None
+    # every config: forward, backward and fwd+bwd TFLOP/s, valid and padded FLOPs
+    configs = {}
+    if args.configs not in ("", "none"):
+        for key in args.configs.split(","):
+            name, _, scale = key.partition("@")
+            if name == args.workload and not scale:
+                res = main_res
+            elif pad_res is not None and name == args.pad_workload and not scale:
+                res = pad_res
+            else:
+                res = run_gpu(name, args.steps, args.warmup, qk_scale=float(scale) if scale else None)
+            configs[key] = config_record(res)
     w = main_res["workload"]
     dom_name = max(main_res["kernels"], key=lambda k: main_res["kernels"][k]["ms"])
     dom = main_res["kernels"][dom_name]
@@ -411,6 +498,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         line["copy_bytes"] = args.copy_bytes
+    if configs:
+        line["configs"] = configs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

@@ -54,20 +54,27 @@ import math
 
 import numpy as np
 
+# Arithmetic the oracle can run in. float64 is the oracle: every parity check
+# and pin uses it. float32 is a timing mode for the CPU baseline only (the
+# same steps in single precision, a fairer CPU number than float64).
+TIMING_DTYPES = (np.float64, np.float32)
+
 # Rows per dense block when a head is too large to hold its full n_q x n_k
 # score matrix. Each block is the dense definition applied to a slice of
 # independent rows, so no sum is split or reordered.
 _MAX_BLOCK_ELEMS = 1 << 24
 
 
-def sigmoid(x):
+def sigmoid(x, dtype=np.float64):
     """Logistic function sigma(x) = 1 / (1 + e^{-x}), elementwise, float64.
 
     The formula is the one in the gist.science summary, section 2.A. It is
     evaluated in the two algebraically equal forms that never overflow:
     1 / (1 + e^{-x}) for x >= 0 and e^{x} / (1 + e^{x}) for x < 0.
+    dtype float32 is the CPU-timing mode (see TIMING_DTYPES); every check
+    uses float64.
     """
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=dtype)
     out = np.empty_like(x)
     pos = x >= 0
     out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
@@ -76,27 +83,27 @@ def sigmoid(x):
     return out
 
 
-def scores(qv, kv, alpha, bias):
+def scores(qv, kv, alpha, bias, dtype=np.float64):
     """Scores S = alpha * Q K^T + b for one (sample, head), valid rows only.
 
     From the rainbus.top summary, "方法步骤详情" step 2, and the gist.science
     summary, section 2.A. qv is [n_q, D] and kv is [n_k, D]. Returns [n_q, n_k].
     """
-    return alpha * (np.asarray(qv, np.float64) @ np.asarray(kv, np.float64).T) + bias
+    return dtype(alpha) * (np.asarray(qv, dtype) @ np.asarray(kv, dtype).T) + dtype(bias)
 
 
-def head_forward(qv, kv, vv, alpha, bias):
+def head_forward(qv, kv, vv, alpha, bias, dtype=np.float64):
     """O = sigma(S) V for one (sample, head) on its valid rows.
 
     From the rainbus.top summary, "方法步骤详情" steps 2-3. There is no row
     normalisation: each weight is an independent sigmoid (paperlayer.ai
     summary, section 3).
     """
-    p = sigmoid(scores(qv, kv, alpha, bias))
-    return p @ np.asarray(vv, np.float64)
+    p = sigmoid(scores(qv, kv, alpha, bias, dtype=dtype), dtype=dtype)
+    return p @ np.asarray(vv, dtype)
 
 
-def head_backward(qv, kv, vv, dov, alpha, bias, return_intermediates=False):
+def head_backward(qv, kv, vv, dov, alpha, bias, return_intermediates=False, dtype=np.float64):
     """Gradients of O = sigma(alpha Q K^T + b) V for one (sample, head).
 
     The forward is recomputed (P = sigma(S)), as in the rainbus.top summary,
@@ -108,16 +115,16 @@ def head_backward(qv, kv, vv, dov, alpha, bias, return_intermediates=False):
       dV = P^T dO                              (chain rule)
     All inputs cover valid rows only: qv, dov are [n_q, D]; kv, vv are [n_k, D].
     """
-    qv = np.asarray(qv, np.float64)
-    kv = np.asarray(kv, np.float64)
-    vv = np.asarray(vv, np.float64)
-    dov = np.asarray(dov, np.float64)
-    s = scores(qv, kv, alpha, bias)
-    p = sigmoid(s)
+    qv = np.asarray(qv, dtype)
+    kv = np.asarray(kv, dtype)
+    vv = np.asarray(vv, dtype)
+    dov = np.asarray(dov, dtype)
+    s = scores(qv, kv, alpha, bias, dtype=dtype)
+    p = sigmoid(s, dtype=dtype)
     dp = dov @ vv.T
     ds = p * (1.0 - p) * dp
-    dq = alpha * (ds @ kv)
-    dk = alpha * (ds.T @ qv)
+    dq = dtype(alpha) * (ds @ kv)
+    dk = dtype(alpha) * (ds.T @ qv)
     dv = p.T @ dov
     if return_intermediates:
         return dq, dk, dv, {"S": s, "P": p, "dP": dp, "dS": ds}
@@ -167,29 +174,30 @@ def _row_blocks(n_rows, n_other):
     return [(s, min(s + step, n_rows)) for s in range(0, n_rows, step)]
 
 
-def forward(q, k, v, seqlens_q, seqlens_k, alpha, bias):
+def forward(q, k, v, seqlens_q, seqlens_k, alpha, bias, dtype=np.float64):
     """Padding-aware forward over the whole batch: O[z, :, h, :] for every z, h.
 
     Q, K, V are [Z, L, H, D] (rainbus.top summary, "方法步骤详情" step 1).
     For sample z only the prefixes Q[z, :n_q[z]], K[z, :n_k[z]] and
     V[z, :n_k[z]] are read. Rows i >= n_q[z] of O are 0. bias is one scalar
-    or Z per-sample values (see per_sample_bias). Returns float64.
+    or Z per-sample values (see per_sample_bias). Returns float64 (dtype:
+    the CPU-timing mode, see TIMING_DTYPES).
     """
     Z, L, H, D = _check_qkv(q, k, v)
     nq = _check_lengths(seqlens_q, Z, L, "seqlens_q")
     nk = _check_lengths(seqlens_k, Z, L, "seqlens_k")
-    o = np.zeros((Z, L, H, D), np.float64)
+    o = np.zeros((Z, L, H, D), dtype)
     for z in range(Z):
         a, b = int(nq[z]), int(nk[z])
         for h in range(H):
             kv = k[z, :b, h, :]
             vv = v[z, :b, h, :]
             for r0, r1 in _row_blocks(a, b):
-                o[z, r0:r1, h, :] = head_forward(q[z, r0:r1, h, :], kv, vv, alpha, _bias_at(bias, z, Z))
+                o[z, r0:r1, h, :] = head_forward(q[z, r0:r1, h, :], kv, vv, alpha, _bias_at(bias, z, Z), dtype=dtype)
     return o
 
 
-def backward(q, k, v, do, seqlens_q, seqlens_k, alpha, bias):
+def backward(q, k, v, do, seqlens_q, seqlens_k, alpha, bias, dtype=np.float64):
     """Padding-aware backward over the whole batch. Returns (dQ, dK, dV), float64.
 
     Each dQ row depends on its own query row and on all valid keys, so dQ is
@@ -203,18 +211,18 @@ def backward(q, k, v, do, seqlens_q, seqlens_k, alpha, bias):
         raise ValueError("do must be [Z, L, H, D]")
     nq = _check_lengths(seqlens_q, Z, L, "seqlens_q")
     nk = _check_lengths(seqlens_k, Z, L, "seqlens_k")
-    dq = np.zeros((Z, L, H, D), np.float64)
-    dk = np.zeros((Z, L, H, D), np.float64)
-    dv = np.zeros((Z, L, H, D), np.float64)
+    dq = np.zeros((Z, L, H, D), dtype)
+    dk = np.zeros((Z, L, H, D), dtype)
+    dv = np.zeros((Z, L, H, D), dtype)
     for z in range(Z):
         a, b = int(nq[z]), int(nk[z])
         for h in range(H):
             qv, kv, vv, dov = q[z, :a, h, :], k[z, :b, h, :], v[z, :b, h, :], do[z, :a, h, :]
             bz = _bias_at(bias, z, Z)
             for r0, r1 in _row_blocks(a, b):
-                dq[z, r0:r1, h, :] = head_backward(qv[r0:r1], kv, vv, dov[r0:r1], alpha, bz)[0]
+                dq[z, r0:r1, h, :] = head_backward(qv[r0:r1], kv, vv, dov[r0:r1], alpha, bz, dtype=dtype)[0]
             for c0, c1 in _row_blocks(b, a):
-                _, dkb, dvb = head_backward(qv, kv[c0:c1], vv[c0:c1], dov, alpha, bz)
+                _, dkb, dvb = head_backward(qv, kv[c0:c1], vv[c0:c1], dov, alpha, bz, dtype=dtype)
                 dk[z, c0:c1, h, :] = dkb
                 dv[z, c0:c1, h, :] = dvb
     return dq, dk, dv

@@ -5,8 +5,9 @@
     python -m padding_aware_sigmoid_amd.profiling traffic  --fetch DIR --write DIR --workload NAME
                                                            --copy-bytes N [-o OUT.json]
 
-`stats` tabulates a `--kernel-trace --stats` run (per-kernel calls and
-durations). `counters` tabulates `--pmc` runs: each counter's mean per
+`stats` tabulates a `--kernel-trace --stats` run: per kernel and grid size
+(one workload's launches), calls, mean, the warm median (every dispatch but
+the first, cold one), min and max; then rocprofv3's own per-kernel stats. `counters` tabulates `--pmc` runs: each counter's mean per
 dispatch, per kernel. `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run
 into HBM bytes per launch. Each counter is scaled by the factor that makes it
 read the known size of a plain device copy recorded in the same run
@@ -95,6 +96,41 @@ def stats_table(trace_dir: pathlib.Path) -> str:
         name = short_name(r["Name"]) or r["Name"][:48]
         out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | {float(r['MinNs']) / 1e6:.4f} | "
                    f"{float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(out)
+
+
+def _grid(r: dict) -> int:
+    for key in ("Grid_Size_X", "Grid_Size", "Grid_SizeX"):
+        if key in r and r[key] not in ("", None):
+            return int(r[key])
+    return 0
+
+
+def trace_groups(trace_dir: pathlib.Path) -> dict:
+    """Per-dispatch durations (ns, in start order) from a --kernel-trace run,
+    keyed by (kernel name, grid size): one workload's launches of a kernel
+    share a grid size, so the same kernel run on two workloads falls into two
+    groups."""
+    groups: dict = {}
+    for r in sorted(_csv(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        name = short_name(r["Kernel_Name"]) or r["Kernel_Name"][:48]
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault((name, _grid(r)), []).append(dur)
+    return groups
+
+
+def trace_table(trace_dir: pathlib.Path) -> str:
+    """Calls, mean, warm median (every dispatch but the group's first, which
+    is cold), min and max per (kernel, grid size)."""
+    out = ["| kernel | grid (work-items) | calls | avg ms | warm median ms | min ms | max ms |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    rows = []
+    for (name, grid), d in trace_groups(trace_dir).items():
+        warm = sorted(d[1:]) if len(d) > 1 else list(d)
+        med = warm[len(warm) // 2] if len(warm) % 2 else 0.5 * (warm[len(warm) // 2 - 1] + warm[len(warm) // 2])
+        rows.append((sum(d), f"| {name} | {grid} | {len(d)} | {sum(d) / len(d) / 1e6:.4f} | {med / 1e6:.4f} | "
+                             f"{min(d) / 1e6:.4f} | {max(d) / 1e6:.4f} |"))
+    out += [r for _, r in sorted(rows, key=lambda x: -x[0])]
     return "\n".join(out)
 
 
@@ -197,7 +233,10 @@ def main(argv=None):
     t.add_argument("-o", type=pathlib.Path)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
-        text = stats_table(args.trace_dir)
+        try:
+            text = trace_table(args.trace_dir) + "\n\n" + stats_table(args.trace_dir)
+        except FileNotFoundError:
+            text = stats_table(args.trace_dir)
     elif args.cmd == "counters":
         text = counters_table(args.pmc_dirs)
     else:

@@ -97,7 +97,7 @@ def _varlen_fwd(variant):
 def _hb(variant):
     """A head_backward with one planted mistake."""
 
-    def f(qv, kv, vv, dov, alpha, bias, return_intermediates=False):
+    def f(qv, kv, vv, dov, alpha, bias, return_intermediates=False, dtype=np.float64):
         qv, kv, vv, dov = (np.asarray(t, np.float64) for t in (qv, kv, vv, dov))
         s = osa.scores(qv, kv, alpha, bias)
         p = osa.sigmoid(s)
@@ -128,7 +128,7 @@ def _hb(variant):
 def _forward_mask(variant):
     """A full-batch forward that gets the padding wrong."""
 
-    def f(q, k, v, seqlens_q, seqlens_k, alpha, bias):
+    def f(q, k, v, seqlens_q, seqlens_k, alpha, bias, dtype=np.float64):
         Z, L, H, D = np.asarray(q).shape
         nq = np.asarray(seqlens_q).astype(int)
         nk = np.asarray(seqlens_k).astype(int)
@@ -144,7 +144,7 @@ def _forward_mask(variant):
 
 
 def _backward_mask(variant):
-    def f(q, k, v, do, seqlens_q, seqlens_k, alpha, bias):
+    def f(q, k, v, do, seqlens_q, seqlens_k, alpha, bias, dtype=np.float64):
         Z, L, H, D = np.asarray(q).shape
         nq = np.asarray(seqlens_q).astype(int)
         nk = np.asarray(seqlens_k).astype(int)
@@ -217,14 +217,14 @@ _orig_fp8_forward = f8a.forward
 
 
 MUTANTS = {
-    "bias dropped": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(kv, float).T)),
-    "alpha dropped": ("scores", lambda qv, kv, a, b: (np.asarray(qv, float) @ np.asarray(kv, float).T) + b),
-    "bias sign": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(kv, float).T) - b),
-    "scores use Q Q^T": ("scores", lambda qv, kv, a, b: a * (np.asarray(qv, float) @ np.asarray(qv, float).T[:, : np.asarray(kv).shape[0]]) + b
+    "bias dropped": ("scores", lambda qv, kv, a, b, dtype=np.float64: a * (np.asarray(qv, float) @ np.asarray(kv, float).T)),
+    "alpha dropped": ("scores", lambda qv, kv, a, b, dtype=np.float64: (np.asarray(qv, float) @ np.asarray(kv, float).T) + b),
+    "bias sign": ("scores", lambda qv, kv, a, b, dtype=np.float64: a * (np.asarray(qv, float) @ np.asarray(kv, float).T) - b),
+    "scores use Q Q^T": ("scores", lambda qv, kv, a, b, dtype=np.float64: a * (np.asarray(qv, float) @ np.asarray(qv, float).T[:, : np.asarray(kv).shape[0]]) + b
                          if np.asarray(qv).shape[0] >= np.asarray(kv).shape[0] else _orig_scores(qv, kv, a, b) * 1.01),
-    "sigma sign": ("sigmoid", lambda x: _orig_sigmoid(-np.asarray(x, float))),
-    "sigma of 2x (tanh slip)": ("sigmoid", lambda x: _orig_sigmoid(2.0 * np.asarray(x, float))),
-    "sigma without exp": ("sigmoid", lambda x: 1.0 / (1.0 + np.abs(np.asarray(x, float)))),
+    "sigma sign": ("sigmoid", lambda x, dtype=np.float64: _orig_sigmoid(-np.asarray(x, float))),
+    "sigma of 2x (tanh slip)": ("sigmoid", lambda x, dtype=np.float64: _orig_sigmoid(2.0 * np.asarray(x, float))),
+    "sigma without exp": ("sigmoid", lambda x, dtype=np.float64: 1.0 / (1.0 + np.abs(np.asarray(x, float)))),
     "dS drops (1-P)": ("head_backward", _hb("dS drops (1-P)")),
     "dS sign": ("head_backward", _hb("dS sign")),
     "dP uses K": ("head_backward", _hb("dP uses K")),
