@@ -703,12 +703,19 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
           iteration(sQ2, sG2, sS2, sQ1, sG1, sQ0, sG0, sS0, u + 1, nqt);
           iteration(sQ0, sG0, sS0, sQ2, sG2, sQ1, sG1, sS1, u + 2, nqt);
         }
-        // The leftover iterations take their slots through lds_opaque: the
-        // compiler then neither shares their LDS addresses with the loop's
-        // (sharing them cost the loop 40 address adds per round) nor waits
-        // for their DMA on its own; each iteration waits for it itself
-        // (dma_wait and the barrier at its top).
-        auto o = [](auto* x) { return lds_opaque(x); };
+        // At D = 128 the leftover iterations take their slots through
+        // lds_opaque: the compiler then neither shares their LDS addresses
+        // with the loop's (sharing them cost the loop 40 address adds per
+        // round) nor waits for their DMA on its own; each iteration waits for
+        // it itself (dma_wait and the barrier at its top). At D = 64 the
+        // opaque form left 8 more spill accesses in the loop (cellbatch8k
+        // dK/dV 4% slower), and named slots leave the loop as it was.
+        auto o = [](auto* x) {
+          if constexpr (D == 128)
+            return lds_opaque(x);
+          else
+            return x;
+        };
         if (ni3 < ni) iteration(o(sQ1), o(sG1), o(sS1), o(sQ0), o(sG0), o(sQ2), o(sG2), o(sS2), ni3 + 1, nqt);
         if (ni3 + 1 < ni) iteration(o(sQ2), o(sG2), o(sS2), o(sQ1), o(sG1), o(sQ0), o(sG0), o(sS0), ni3 + 2, nqt);
         // The last tile's B and V stages, in its slot (nqt - 1) mod 3, named at
