@@ -327,31 +327,30 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // DMA ROWS rows into a swizzled LDS tile. The tile's row i starts at byte
 // i * row_bytes after `rows` (row 0 of the tile in global memory). Rows at or
-// past n_valid are never read: their lanes take an out-of-range offset, so
-// the LDS receives zeros. The buffer resource covers only the valid rows, so
-// every offset stays below ROWS * row_bytes. Every wave of the workgroup takes
-// part. Call dma_wait() before the barrier that publishes the tile.
-template <int D, int ROWS, int NTHREADS>
-__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid, int tid) {
+// past n_valid are never read: their lanes lie past the end of the buffer
+// resource, so the LDS receives zeros. Every wave of the workgroup takes part.
+// Call dma_wait() before the barrier that publishes the tile.
+//
+// The tile moves in chunks of NTHREADS 16-byte slots, RPC = NTHREADS / CPR
+// whole rows each. A lane's slot in a chunk sits at the same row within the
+// chunk and the same swizzled column in every chunk (RPC is a multiple of the
+// swizzle's row period), so its byte offset dma_lane_offset() is one value
+// per kernel. Each chunk gets its own buffer resource: based at the chunk's
+// first row and ending at the last valid row in it (none if the chunk lies
+// wholly past n_valid). Only scalar work changes from chunk to chunk.
+template <int D, int NTHREADS>
+constexpr int kDmaRowsPerChunk = NTHREADS / Tile<D>::CPR;
+
+template <int D, int NTHREADS>
+__device__ __forceinline__ uint32_t dma_lane_offset(uint32_t row_bytes, int tid) {
   constexpr int CPR = Tile<D>::CPR;
-  constexpr int SLOTS = ROWS * CPR;
-  static_assert(SLOTS % NTHREADS == 0, "tile must split evenly over the workgroup");
-  const int nv = n_valid < 0 ? 0 : (n_valid > ROWS ? ROWS : n_valid);
-  const i32x4 rsrc = make_rsrc(rows, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
-  const int lane = tid & 63, wbase = tid & ~63;
-#pragma unroll
-  for (int i = 0; i < SLOTS / NTHREADS; ++i) {
-    const int P0 = i * NTHREADS + wbase;  // wave-uniform first slot
-    const int P = P0 + lane;
-    const int r = P / CPR, cs = P % CPR;
-    const int c = cs ^ Tile<D>::swz(r);
-    const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
-    llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16),
-                                    16, (int)voff, 0, 0, 0);
-  }
+  static_assert(NTHREADS % CPR == 0 && kDmaRowsPerChunk<D, NTHREADS> % 16 == 0,
+                "chunks must hold whole rows and a whole number of swizzle periods");
+  const int r = tid / CPR, c = (tid % CPR) ^ Tile<D>::swz(r);
+  return (uint32_t)r * row_bytes + ((uint32_t)c << 4);
 }
 
-// One of dma_tile's (ROWS * D / 8) / NTHREADS DMA instructions per thread,
+// One of a tile's (ROWS * D / 8) / NTHREADS DMA instructions per thread,
 // chunk i, so that a tile's DMA can be spread over a step schedule instead of
 // issued in one burst. Calling every i in 0 .. kDmaChunks - 1 equals dma_tile.
 template <int D, int ROWS, int NTHREADS>
@@ -360,17 +359,23 @@ constexpr int kDmaChunks = ROWS * Tile<D>::CPR / NTHREADS;
 template <int D, int ROWS, int NTHREADS>
 __device__ __forceinline__ void dma_tile_chunk(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid,
                                                int tid, int i) {
-  constexpr int CPR = Tile<D>::CPR;
-  const int nv = n_valid < 0 ? 0 : (n_valid > ROWS ? ROWS : n_valid);
-  const i32x4 rsrc = make_rsrc(rows, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
-  const int lane = tid & 63, wbase = tid & ~63;
-  const int P0 = i * NTHREADS + wbase;  // wave-uniform first slot
-  const int P = P0 + lane;
-  const int r = P / CPR, cs = P % CPR;
-  const int c = cs ^ Tile<D>::swz(r);
-  const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16), 16,
-                                  (int)voff, 0, 0, 0);
+  constexpr int RPC = kDmaRowsPerChunk<D, NTHREADS>;
+  static_assert(ROWS % RPC == 0, "tile must split evenly over the workgroup");
+  const int nvi = n_valid - i * RPC;
+  const int nv = nvi < 0 ? 0 : (nvi > RPC ? RPC : nvi);
+  const char* base = (const char*)rows + (size_t)(i * RPC) * row_bytes;
+  const i32x4 rsrc = make_rsrc(base, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
+  const int wbase = __builtin_amdgcn_readfirstlane(tid) & ~63;  // wave-uniform first slot of the chunk
+  llvm_amdgcn_raw_buffer_load_lds(
+      rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + (i * NTHREADS + wbase) * 16), 16,
+      (int)dma_lane_offset<D, NTHREADS>(row_bytes, tid), 0, 0, 0);
+}
+
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid, int tid) {
+#pragma unroll
+  for (int i = 0; i < kDmaChunks<D, ROWS, NTHREADS>; ++i)
+    dma_tile_chunk<D, ROWS, NTHREADS>(tile, rows, row_bytes, n_valid, tid, i);
 }
 
 // DMA 64 rows of a float2 row statistic into LDS as float2[64] (512 B). Row r

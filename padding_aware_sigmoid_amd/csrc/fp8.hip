@@ -115,23 +115,28 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// DMA 64 rows of D bytes into a swizzled LDS tile; rows at or past n_valid arrive as zeros.
+// DMA 64 rows of D bytes into a swizzled LDS tile; rows at or past n_valid arrive
+// as zeros because they lie past the end of the buffer resource. As for the bf16
+// tiles, the tile moves in chunks of 256 16-byte slots (RPC whole rows each); a
+// lane's offset within its chunk is the same in every chunk (RPC is a multiple
+// of the swizzle's 16-row period), and each chunk has its own resource, based
+// at its first row and ending at its last valid row.
 template <int D>
 __device__ __forceinline__ void dma_tile8(uint8_t* tile, const uint8_t* rows, uint32_t row_bytes, int n_valid,
                                           int tid) {
-  constexpr int CPR = D / 16, SLOTS = 64 * CPR;
-  const int nv = n_valid < 0 ? 0 : (n_valid > 64 ? 64 : n_valid);
-  const i32x4 rsrc = make_rsrc(rows, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + D : 0u);
-  const int lane = tid & 63, wbase = tid & ~63;
+  constexpr int CPR = D / 16, RPC = 256 / CPR;
+  static_assert(64 % RPC == 0 && RPC % 16 == 0, "chunks must hold whole swizzle periods and split the tile");
+  const int r0 = tid / CPR, c0 = (tid % CPR) ^ f8_swz<D>(r0);
+  const uint32_t voff = (uint32_t)r0 * row_bytes + ((uint32_t)c0 << 4);
+  const int wbase = __builtin_amdgcn_readfirstlane(tid) & ~63;
 #pragma unroll
-  for (int i = 0; i < SLOTS / 256; ++i) {
-    const int P0 = i * 256 + wbase;
-    const int P = P0 + lane;
-    const int r = P / CPR, cs = P % CPR;
-    const int c = cs ^ f8_swz<D>(r);
-    const uint32_t voff = r < nv ? (uint32_t)r * row_bytes + ((uint32_t)c << 4) : kOutOfRange;
-    llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + P0 * 16),
-                                    16, (int)voff, 0, 0, 0);
+  for (int i = 0; i < 64 / RPC; ++i) {
+    const int nvi = n_valid - i * RPC;
+    const int nv = nvi < 0 ? 0 : (nvi > RPC ? RPC : nvi);
+    const i32x4 rsrc = make_rsrc(rows + (size_t)(i * RPC) * row_bytes, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + D : 0u);
+    llvm_amdgcn_raw_buffer_load_lds(
+        rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + (i * 256 + wbase) * 16), 16, (int)voff, 0,
+        0, 0);
   }
 }
 
