@@ -250,23 +250,32 @@ __device__ __forceinline__ void pin_before_barrier(bf16x8 (&p)[2][2]) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of D bf16, stored unpadded in 16-byte chunks with an XOR
-// swizzle. Physical chunk slot = logical chunk ^ swz(row). The swizzle makes
-// both operand reads conflict-free:
-//  - a natural read: 16 lanes, 16 consecutive rows, one chunk each;
-//  - a transposed read (ds_read_b64_tr_b16): 32 lanes, 4 consecutive rows,
-//    4 consecutive chunks.
-// It also lets whole tiles arrive by DMA (global -> LDS, 1 KB contiguous per
-// wave instruction), since no padding is needed.
+// LDS tiles: 64 rows of D bf16, unpadded. The tile is stored as D / 32 column
+// blocks, one after the other; a block holds the 32 columns of every row as
+// 64-byte row pieces (four 16-byte chunks), and within a piece the physical
+// chunk is the logical one XOR swz(row) = (row >> 2) & 3. Both operand reads
+// are conflict-free (16-byte bank groups, 256 bytes per LDS phase):
+//  - a natural read (16 lanes, 16 consecutive rows, one chunk each) covers
+//    every (row % 4, physical chunk) pair once;
+//  - a transposed read (ds_read_b64_tr_b16: 32 lanes, 4 consecutive rows of
+//    one block, starting at a multiple of 4) reads 256 contiguous bytes.
+// The layout is chosen so that operands at another column block, or 16 rows
+// further down, lie at a constant byte distance from the same lane's address:
+// only two lane patterns exist per read kind (chunk bit 1 clear or set for
+// natural reads, row bit 3 clear or set for transposed reads), and every other
+// operand address is one of them plus an immediate offset.
+// Whole tiles still arrive by DMA: one column block is 256 16-byte slots, the
+// 1 KB per wave instruction of a 256-thread workgroup landing contiguously.
 template <int D>
 struct Tile {
+  static constexpr int ROWS = 64;
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  __device__ static __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
+  static constexpr int BLOCK_BYTES = ROWS * 64;
+  __device__ static __forceinline__ int swz(int r) { return (r >> 2) & 3; }
   // byte offset of logical chunk c of row r
-  __device__ static __forceinline__ int off(int r, int c) { return (r * CPR + (c ^ swz(r))) << 4; }
+  __device__ static __forceinline__ int off(int r, int c) {
+    return (c >> 2) * BLOCK_BYTES + ((r * 4 + ((c & 3) ^ swz(r))) << 4);
+  }
 };
 
 // Natural operand: 8 consecutive values of row r starting at logical chunk c.
@@ -325,49 +334,45 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// DMA ROWS rows into a swizzled LDS tile. The tile's row i starts at byte
+// DMA a tile's ROWS = 64 rows into LDS. The tile's row i starts at byte
 // i * row_bytes after `rows` (row 0 of the tile in global memory). Rows at or
 // past n_valid are never read: their lanes lie past the end of the buffer
-// resource, so the LDS receives zeros. Every wave of the workgroup takes part.
-// Call dma_wait() before the barrier that publishes the tile.
+// resource, which ends at the last valid row, so the LDS receives zeros.
+// Every wave of the workgroup takes part. Call dma_wait() before the barrier
+// that publishes the tile.
 //
-// The tile moves in chunks of NTHREADS 16-byte slots, RPC = NTHREADS / CPR
-// whole rows each. A lane's slot in a chunk sits at the same row within the
-// chunk and the same swizzled column in every chunk (RPC is a multiple of the
-// swizzle's row period), so its byte offset dma_lane_offset() is one value
-// per kernel. Each chunk gets its own buffer resource: based at the chunk's
-// first row and ending at the last valid row in it (none if the chunk lies
-// wholly past n_valid). Only scalar work changes from chunk to chunk.
-template <int D, int NTHREADS>
-constexpr int kDmaRowsPerChunk = NTHREADS / Tile<D>::CPR;
-
+// Chunk i moves column block i: thread t fetches row t / 4, physical chunk
+// t % 4 of that block (1 KB contiguous in LDS per wave). A thread's offset
+// within the block, dma_lane_offset(), is the same for every block; the
+// block's 64-byte column shift goes into the chunk's buffer resource (base
+// moved by 64 * i bytes, range shortened by as much), so only scalar work and
+// no per-lane arithmetic is left per tile. (The instruction's immediate
+// offset cannot carry the shift: the DMA adds it to the LDS address too.)
 template <int D, int NTHREADS>
 __device__ __forceinline__ uint32_t dma_lane_offset(uint32_t row_bytes, int tid) {
-  constexpr int CPR = Tile<D>::CPR;
-  static_assert(NTHREADS % CPR == 0 && kDmaRowsPerChunk<D, NTHREADS> % 16 == 0,
-                "chunks must hold whole rows and a whole number of swizzle periods");
-  const int r = tid / CPR, c = (tid % CPR) ^ Tile<D>::swz(r);
+  static_assert(NTHREADS == 4 * Tile<D>::ROWS, "one wave instruction per thread moves one column block");
+  const int r = tid >> 2, c = (tid & 3) ^ Tile<D>::swz(r);
   return (uint32_t)r * row_bytes + ((uint32_t)c << 4);
 }
 
-// One of a tile's (ROWS * D / 8) / NTHREADS DMA instructions per thread,
-// chunk i, so that a tile's DMA can be spread over a step schedule instead of
+// One of a tile's D / 32 DMA instructions per thread, chunk i (column block
+// i), so that a tile's DMA can be spread over a step schedule instead of
 // issued in one burst. Calling every i in 0 .. kDmaChunks - 1 equals dma_tile.
 template <int D, int ROWS, int NTHREADS>
-constexpr int kDmaChunks = ROWS * Tile<D>::CPR / NTHREADS;
+constexpr int kDmaChunks = D / 32;
 
 template <int D, int ROWS, int NTHREADS>
 __device__ __forceinline__ void dma_tile_chunk(__bf16* tile, const __bf16* rows, uint32_t row_bytes, int n_valid,
                                                int tid, int i) {
-  constexpr int RPC = kDmaRowsPerChunk<D, NTHREADS>;
-  static_assert(ROWS % RPC == 0, "tile must split evenly over the workgroup");
-  const int nvi = n_valid - i * RPC;
-  const int nv = nvi < 0 ? 0 : (nvi > RPC ? RPC : nvi);
-  const char* base = (const char*)rows + (size_t)(i * RPC) * row_bytes;
-  const i32x4 rsrc = make_rsrc(base, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D : 0u);
+  static_assert(ROWS == Tile<D>::ROWS, "tiles are 64 rows");
+  const int nv = n_valid < 0 ? 0 : (n_valid > ROWS ? ROWS : n_valid);
+  // Valid rows end at byte (nv - 1) * row_bytes + 2 * D of the tile; block i
+  // starts at byte 64 * i of each row (64 * i < 2 * D).
+  const i32x4 rsrc =
+      make_rsrc((const char*)rows + 64 * i, nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 2 * D - 64 * i : 0u);
   const int wbase = __builtin_amdgcn_readfirstlane(tid) & ~63;  // wave-uniform first slot of the chunk
   llvm_amdgcn_raw_buffer_load_lds(
-      rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + (i * NTHREADS + wbase) * 16), 16,
+      rsrc, (lds_u32_ptr)((__attribute__((address_space(3))) char*)tile + i * Tile<D>::BLOCK_BYTES + wbase * 16), 16,
       (int)dma_lane_offset<D, NTHREADS>(row_bytes, tid), 0, 0, 0);
 }
 
