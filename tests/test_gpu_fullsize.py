@@ -7,6 +7,24 @@ The sampled rows always include rows 0 and 1, tile edges, n-1, n (the first
 padded row) and L-1, plus random rows. Every sampled padded row must be
 exactly 0. The skip decisions (tile counters) are compared in full with the
 oracle's tile plan.
+
+Two bounds hold every sampled output:
+* the global one, max|got - ref| / max|ref| <= 2e-2;
+* a second, elementwise one derived from the kernels' arithmetic. Inputs are
+  bf16 and exact in both; each product term of a contraction carries one bf16
+  rounding of its weight (P for O and dV, dS for dQ and dK; relative error at
+  most u = 2^-8, taken as independent and uniform, so their sum has standard
+  deviation at most (u / sqrt 3) sqrt(sum w^2 x^2)); the sums run in fp32
+  (error modelled the same way with 2^-24 per step over n terms); the result
+  is rounded to bf16 once (at most u |ref|). The bound is
+      1.01 u |ref| + 6 (u / sqrt 3) sqrt(sum_j w_j^2 x_j^2)
+                   + 6 * 2^-24 sqrt(n) sum_j |w_j x_j|
+  per element, with w, x the weight and operand of the contraction. Six
+  standard deviations over the few thousand sampled elements of a run leave
+  a chance of a false failure far below 1e-6. For O at 16K keys its largest
+  value is about 1e-2 of max|ref|, and every element is held to its own
+  scale; an emulation of these roundings on the CPU stays within half of it,
+  and dropping one block of 16 keys exceeds it about eightfold.
 """
 
 import numpy as np
@@ -20,6 +38,18 @@ from gpu_util import device_inputs, note, rel_err
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
+U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits)
+U_FP32 = 2.0 ** -24
+N_SIGMA = 6.0
+
+
+def _derived_bound(ref, w, x, scale=1.0):
+    """Elementwise bound on |got - ref| for ref = scale * w @ x (w: [rows, n], x: [n, D])."""
+    n = w.shape[1]
+    stat = np.sqrt((w * w) @ (x * x))
+    absum = np.abs(w) @ np.abs(x)
+    return (1.01 * U_BF16 * np.abs(ref) + scale * N_SIGMA * (U_BF16 / np.sqrt(3.0)) * stat
+            + scale * N_SIGMA * U_FP32 * np.sqrt(max(n, 1)) * absum)
 
 
 def _sample_rows(n, L, rng):
@@ -57,23 +87,49 @@ def _run_full(name, qk_scale=None, heads_per_sample=2, seed=0):
     rng = np.random.default_rng(1234)
     got = {k: [] for k in outs}
     ref = {k: [] for k in outs}
+    bnd = {k: [] for k in outs}
     for z in range(w.Z):
         heads = sorted({0, w.H - 1, int(rng.integers(0, w.H))})[:max(1, heads_per_sample)]
         qrows = _sample_rows(int(nq[z]), w.L, rng)
         krows = _sample_rows(int(nk[z]), w.L, rng)
+        a, b = int(nq[z]), int(nk[z])
+        bz = w.bias[z] if np.ndim(w.bias) else w.bias
         for h in heads:
             o_ref = oracle.forward_rows(Q, K, V, nq, nk, w.alpha, w.bias, z, h, qrows)
             dq_ref, dk_ref, dv_ref = oracle.backward_rows(Q, K, V, DO, nq, nk, w.alpha, w.bias, z, h, qrows, krows)
-            for key, rows, r in (("O", qrows, o_ref), ("dQ", qrows, dq_ref), ("dK", krows, dk_ref),
-                                 ("dV", krows, dv_ref)):
+            # Weights of the sampled rows' contractions (P and dS), from the oracle on the same slices
+            # that backward_rows solves; padded rows have no terms and a bound of 0.
+            bo = np.zeros_like(o_ref); bdq = np.zeros_like(dq_ref)
+            bdk = np.zeros_like(dk_ref); bdv = np.zeros_like(dv_ref)
+            lq, lk = qrows < a, krows < b
+            if lq.any():
+                *_, im = oracle.head_backward(Q[z, qrows[lq], h], K[z, :b, h], V[z, :b, h], DO[z, qrows[lq], h],
+                                              w.alpha, bz, return_intermediates=True)
+                bo[lq] = _derived_bound(o_ref[lq], im["P"], V[z, :b, h])
+                bdq[lq] = _derived_bound(dq_ref[lq], im["dS"], K[z, :b, h], w.alpha)
+            if lk.any():
+                *_, im = oracle.head_backward(Q[z, :a, h], K[z, krows[lk], h], V[z, krows[lk], h], DO[z, :a, h],
+                                              w.alpha, bz, return_intermediates=True)
+                bdv[lk] = _derived_bound(dv_ref[lk], im["P"].T, DO[z, :a, h])
+                bdk[lk] = _derived_bound(dk_ref[lk], im["dS"].T, Q[z, :a, h], w.alpha)
+            for key, rows, r, bd in (("O", qrows, o_ref, bo), ("dQ", qrows, dq_ref, bdq), ("dK", krows, dk_ref, bdk),
+                                     ("dV", krows, dv_ref, bdv)):
                 g = outs[key][z, torch.as_tensor(rows, device="cuda"), h].float().cpu().numpy().astype(np.float64)
                 pad = rows >= (nq[z] if key in ("O", "dQ") else nk[z])
                 assert np.all(g[pad] == 0.0), f"{name}: {key} padded sampled row not exactly 0 (z={z})"
                 got[key].append(g)
                 ref[key].append(r)
+                bnd[key].append(bd)
     errs = {k: rel_err(np.concatenate(got[k]), np.concatenate(ref[k])) for k in outs}
     for k, e in errs.items():
         assert e <= BF16_TOL, f"{name} scale={inp['qk_scale']}: {k} sampled rel err {e:.3e} > {BF16_TOL}"
+    for k in outs:
+        g, r, bd = (np.concatenate(x[k]) for x in (got, ref, bnd))
+        ratio = float(np.max(np.abs(g - r) / np.maximum(bd, 1e-300)))
+        tight = float(np.max(bd) / max(float(np.max(np.abs(r))), 1e-300))
+        note(f"{name} scale={inp['qk_scale']} {k}: rel err {errs[k]:.2e}; derived bound {tight:.2e} of max|ref|, "
+             f"worst |err| / bound {ratio:.3f}")
+        assert ratio <= 1.0, f"{name} scale={inp['qk_scale']}: {k} exceeds its derived elementwise bound ({ratio:.3f})"
     del dq_, dk_, dv_, ddo, o, gq, gk, gv
     torch.cuda.empty_cache()
     return errs
