@@ -7,7 +7,7 @@
 * Forward: O against the oracle's quantised forward on the same codes,
   max|GPU - oracle| / max|oracle| <= 2e-2. The two sides differ only where
   fp32 and fp64 scores put a P on opposite sides of an E4M3 rounding boundary
-  (one code step, rare), and in the bf16 rounding of O (2^-9).
+  (one code step, rare), and in the bf16 rounding of O (2^-8 relative).
 * Distance to exact attention. The FP8 oracle encodes this library's own
   quantisation design (the pages fix no FP8 scheme), so the GPU output is
   also held, element by element, to a bound derived from the format against

@@ -5,8 +5,8 @@
   bf16 (2e-2 relative to the largest reference value) and fp32 (1e-5), D = 64
   and 128, lengths that include 0 keys and 0 queries.
 * LSE: bf16 sums the row's P after rounding it to bf16 (so that O is a convex
-  combination of V rows), which moves LSE by at most about 2^-9 relative in
-  the row sum: an absolute 4e-3. fp32: 1e-5.
+  combination of V rows), which moves the row sum by at most 2^-8 relative
+  (bf16's unit roundoff) and LSE by at most 2^-8 absolute: 4e-3. fp32: 1e-5.
 * fp32 gradients: dS = P (dP - D) subtracts numbers of the size of dP, and the
   sums over rows cancel on top, so fp32 rounding is relative to the sums of
   the terms' absolute values, not to the result (on these inputs those sums
