@@ -521,9 +521,15 @@ __device__ __forceinline__ void kv_step(const __bf16* sQa, const __bf16* sGa, in
     // the fused form at D = 128: fences every 1, 2, 4 steps and none, 4.05,
     // 4.08, 4.44, 4.49 ms (L = 16K, H = 16). In the separate dK kernel a fence
     // makes the compiler spill or fail, so it schedules each kv_step as one
-    // region.
+    // region. With the tiles' LDS addresses folded into immediates, the
+    // sigmoid fused form at D = 128 runs best with the fences alone and the
+    // compiler's order within each step (3.93 -> 3.84 ms); softmax and
+    // D = 64 keep the groups (the softmax backward 1.5% slower without them).
     constexpr int FENCE = KB == 1 ? 1 : (MODE == KV_DV ? 2 : kNoFence);
-    sched_step<j, nds, KB, nvalu, FENCE>();
+    if constexpr (D == 128 && ACT == ACT_SIGMOID && MODE == KV_BOTH)
+      sched_fence<j, FENCE>();
+    else
+      sched_step<j, nds, KB, nvalu, FENCE>();
   });
 }
 

@@ -150,6 +150,13 @@ __device__ __forceinline__ void sched_step() {
   if constexpr (J % FENCE == FENCE - 1) __builtin_amdgcn_sched_barrier(0);
 }
 
+// Only the fence of a step: the compiler orders the instructions between two
+// fences itself.
+template <int J, int FENCE>
+__device__ __forceinline__ void sched_fence() {
+  if constexpr (J % FENCE == FENCE - 1) __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ int clamp_len(int n, int L) { return n < 0 ? 0 : (n > L ? L : n); }
 
 // Where each sample's rows live, how many are valid, and the score bias.

@@ -173,7 +173,11 @@ __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, co
       dma_chunk((g - NSTEP) / DSTRIDE);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // the DMA first in its step
     }
-    sched_step<g, reads_of(g + 3), 2, 5 * (e1 - e0), 2>();
+    // At D = 128 the compiler's own order beats the step groups and fences
+    // now that every LDS operand address is a base register plus an
+    // immediate: without them 1.91 -> 1.82 ms (nopad16k). At D = 64 they
+    // stay (within 1% either way).
+    if constexpr (D != 128) sched_step<g, reads_of(g + 3), 2, 5 * (e1 - e0), 2>();
   });
 }
 
