@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void dq_bf16_kernel(const __
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
-  __shared__ int rank_lds[kMaxRankedSamples];
+  __shared__ RankLds rank_lds;
   const int n_qt = (sl.L + C::BQ_DQ - 1) / C::BQ_DQ;
   const TileCoord tcd = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
   const int z = tcd.z, h = tcd.h, m = tcd.m;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(256, MODE == KV_BOTH ? kWavesPerSimd<D> : 1) void d
   __shared__ __attribute__((aligned(64))) float2 sS2[SM && UR ? 64 : 1];
   __shared__ __attribute__((aligned(1024))) __bf16 sRing[UR ? 8 : 6 * C::TILE];
   __shared__ __attribute__((aligned(64))) float2 sSRing[SM && !UR ? 3 * 64 : 1];
-  __shared__ int rank_lds[kMaxRankedSamples];
+  __shared__ RankLds rank_lds;
   constexpr int KT = kKeysPerWg<D, MODE, SWAP>;
   constexpr int WPT = C::BK_KV / KT;  // workgroups per tile of tile_counts
   const int n_kt = (sl.L + C::BK_KV - 1) / C::BK_KV;

@@ -204,18 +204,27 @@ struct SeqLayout {
 // Each XCD then gets a similar share of heavy and light pairs and starts with
 // its heaviest (longest-processing-time first). All tiles of one pair stay on
 // one XCD, so that head's K/V (or Q/dO) stream through one L2.
-// With more than kMaxRankedSamples samples, or when the pair count is not a
-// multiple of 8, the mapping keeps the weight order but drops the XCD dealing.
-// rank_lds must hold kMaxRankedSamples ints. Every thread of the block calls
-// this, and it contains a barrier.
+// With more than kMaxRankedSamples samples the samples keep their index
+// order; when the pair count is not a multiple of 8 the XCD dealing is
+// dropped. Every thread of the block calls this, and it contains two
+// barriers. Each thread t < Z reads its own sample's lengths once and leaves
+// the weight in LDS; the ranks then come from LDS. (Read from global memory
+// inside the ranking loop, each of the 2 Z length reads waited for the one
+// before: microseconds per workgroup at a few dozen samples, paid by every
+// workgroup, the wholly padded ones included.)
 constexpr int kMaxRankedSamples = 256;
+
+struct RankLds {
+  long long weight[kMaxRankedSamples];  // n_q * n_k of sample t
+  int order[kMaxRankedSamples];         // order[rank] = sample
+};
 
 struct TileCoord {
   int z, h, m;
 };
 
 __device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntiles, const SeqLayout& sl,
-                                                   int* rank_lds) {
+                                                   RankLds& rank_lds) {
   const int P = Z * H;
   int p, m;
   if ((P & 7) == 0) {
@@ -230,17 +239,22 @@ __device__ __forceinline__ TileCoord schedule_tile(int b, int Z, int H, int ntil
   int z = r;
   if (Z <= kMaxRankedSamples) {
     const int t = threadIdx.x;
+    long long wt = 0;
     if (t < Z) {
-      const long long wt = (long long)sl.nq(t) * sl.nk(t);
-      int rank = 0;
-      for (int u = 0; u < Z; ++u) {
-        const long long wu = (long long)sl.nq(u) * sl.nk(u);
-        rank += (wu > wt) || (wu == wt && u < t);
-      }
-      rank_lds[rank] = t;
+      wt = (long long)sl.nq(t) * sl.nk(t);
+      rank_lds.weight[t] = wt;
     }
     __syncthreads();
-    z = rank_lds[r];
+    if (t < Z) {
+      int rank = 0;
+      for (int u = 0; u < Z; ++u) {
+        const long long wu = rank_lds.weight[u];
+        rank += (wu > wt) || (wu == wt && u < t);
+      }
+      rank_lds.order[rank] = t;
+    }
+    __syncthreads();
+    z = rank_lds.order[r];
   }
   return {z, h, m};
 }

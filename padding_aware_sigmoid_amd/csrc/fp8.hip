@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_fp8_kernel(const ui
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE];
   __shared__ uint8_t sSK[kF8MaxTiles];
   __shared__ uint8_t sSV[kF8MaxTiles];
-  __shared__ int rank_lds[kMaxRankedSamples];
+  __shared__ RankLds rank_lds;
   const int n_qt = (sl.L + C::BQ - 1) / C::BQ;
   const int ntiles = (sl.L + kF8Tile - 1) / kF8Tile;
   const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void sm_fwd_bf16_kernel(cons
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
-  __shared__ int rank_lds[kMaxRankedSamples];
+  __shared__ RankLds rank_lds;
   const int n_qt = (sl.L + C::BQ - 1) / C::BQ;
   const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
   const int z = tc.z, h = tc.h, m0 = tc.m;
