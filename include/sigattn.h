@@ -32,8 +32,9 @@
  *    above L as L. Padding is a suffix: positions [0, n) are valid.
  *  - Padded input rows are never read, so their contents, NaN included, cannot
  *    change any output.
- *  - Every element of every output is written, padding included. The caller
- *    need not clear outputs.
+ *  - Every element of every output is written, padding included (in the
+ *    packed layout: every row, under the offsets contract at sigattn_fwd_ex).
+ *    The caller need not clear outputs.
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
  *    keeps no reference after the call returns and allocates no memory.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
