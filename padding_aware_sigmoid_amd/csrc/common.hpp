@@ -436,14 +436,4 @@ __device__ __forceinline__ T* lds_opaque(T* p) {
 // Wait until this wave's outstanding global loads (the DMAs included) are done.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
-
-// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8). This remap gives each XCD a contiguous range of logical tile ids.
-// Neighbouring query tiles of one head then share an XCD's L2 and stream the
-// same K/V tiles at about the same time. It is a bijection on [0, n).
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
-  return x * per + (x < rem ? x : rem) + i;
-}
-
 }  // namespace sigattn
