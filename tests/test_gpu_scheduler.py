@@ -10,7 +10,9 @@ These cases cover the three regimes the mapping has:
 The mapping decides only which workgroup computes which tile, so the outputs
 must equal the oracle's whatever it does, with every padded row exactly 0
 (a tile computed twice or never shows there), and the tile counters must
-equal the oracle's tile plan entry for entry.
+equal the oracle's tile plan entry for entry. The softmax kernels and the
+FP8 forward share the mapping; one regime each checks them against their
+oracles.
 """
 
 import numpy as np
@@ -63,3 +65,60 @@ def test_many_samples(Z, H):
         assert e <= TOL, f"{name}: rel err {e:.3e}"
         for z in range(Z):
             assert np.all(gv[z, n[z]:] == 0.0), f"{name}: padded rows of sample {z} not exactly 0"
+
+
+def _lengths(Z, seed):
+    rng = np.random.default_rng(seed)
+    nq, nk = rng.integers(0, L + 1, Z), rng.integers(0, L + 1, Z)
+    nq[:2] = [0, L]
+    nk[:2] = [L, 0]
+    return nq, nk
+
+
+def test_many_samples_softmax():
+    """Softmax forward and backward share the mapping: 300 samples (not ranked, dealt)."""
+    import padding_aware_sigmoid_amd as sa
+
+    Z, H = 300, 2
+    nq, nk = _lengths(Z, 5)
+    note(f"scheduler softmax Z={Z} H={H} L={L} D={D}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=72)
+    dq_, dk_, dv_, ddo, dnq, dnk = device_inputs(q, k, v, do, nq, nk)
+    alpha = 1.0 / np.sqrt(D)
+    o, lse = sa.sigattn_softmax_fwd(dq_, dk_, dv_, dnq, dnk, alpha)
+    g = sa.sigattn_softmax_bwd(dq_, dk_, dv_, o, ddo, lse, dnq, dnk, alpha)
+    torch.cuda.synchronize()
+    SM = oracle.softmax_attention
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    ro, _ = SM.forward(Q, K, V, nq, nk, alpha)
+    refs = (ro,) + SM.backward(Q, K, V, DO, nq, nk, alpha)
+    for name, got, ref, n in zip(("O", "dQ", "dK", "dV"), (o,) + tuple(g), refs, (nq, nq, nk, nk)):
+        gv = host(got)
+        e = rel_err(gv, ref)
+        assert e <= TOL, f"softmax {name}: rel err {e:.3e}"
+        for z in range(Z):
+            assert np.all(gv[z, n[z]:] == 0.0), f"softmax {name}: padded rows of sample {z} not exactly 0"
+
+
+def test_many_samples_fp8():
+    """The FP8 forward shares the mapping: 256 samples (ranked, dealt), against the FP8 oracle."""
+    import padding_aware_sigmoid_amd as sa
+
+    F8 = oracle.fp8_attention
+    Z, H = 256, 8
+    nq, nk = _lengths(Z, 6)
+    note(f"scheduler fp8 Z={Z} H={H} L={L} D={D}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=73)
+    dq_, dk_, dv_, _, dnq, dnk = device_inputs(q, k, v, do, nq, nk)
+    alpha, bias = 1.0 / np.sqrt(D), -np.log(L)
+    q8, sq = sa.sigattn_quantize_fp8(dq_, dnq)
+    k8, sk = sa.sigattn_quantize_fp8(dk_, dnk)
+    v8, sv = sa.sigattn_quantize_fp8(dv_, dnk)
+    o = sa.sigattn_fwd_fp8(q8, k8, v8, sq, sk, sv, dnq, dnk, alpha, bias)
+    torch.cuda.synchronize()
+    ref = F8.forward(*(t.cpu().numpy() for t in (q8, k8, v8, sq, sk, sv)), nq, nk, alpha, bias)
+    gv = host(o)
+    e = rel_err(gv, ref)
+    assert e <= TOL, f"fp8 O: rel err {e:.3e}"
+    for z in range(Z):
+        assert np.all(gv[z, nq[z]:] == 0.0), f"fp8 O: padded rows of sample {z} not exactly 0"
