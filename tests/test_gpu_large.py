@@ -1,0 +1,194 @@
+"""Tensors larger than 4 GiB: every element offset must be 64-bit.
+
+Each case holds Z samples of L = 65536 rows and H = 64 heads, so one sample of
+one tensor spans L * H * D elements and the last sample starts at least
+4 GiB into every bf16 tensor (D = 128: Z = 5, 5 GiB per tensor; D = 64: Z = 9,
+4.5 GiB). Only a few samples have valid rows, a few thousand each, so the
+arithmetic is small while the addresses are not. The inputs outside those
+rows are left as the allocator hands them out: the kernels never read
+padding (the padding tests fill it with NaN and Inf), so whatever it holds
+cannot matter. Checked:
+* the valid rows of O, dQ, dK and dV of the live samples, for three heads
+  each, against the oracle at 2e-2 of max|ref|, and every head finite;
+* every other row of every output exactly 0, to the end of the tensor;
+* the skip decisions (tile counters) against the oracle's tile plan;
+* the softmax path and the FP8 path on the same shapes (D = 128): softmax
+  O and gradients against the softmax oracle, FP8 codes and scale bytes bit
+  for bit against the FP8 oracle's quantiser and the FP8 forward against
+  the FP8 oracle within the derived elementwise bound of tests/fp8_bound.py
+  (the first case here where a global tolerance would not hold: in head 29
+  of sample 3 one key's weight dominates its row and sits on an E4M3
+  rounding tie, so fp32 and float64 pick neighbouring codes and O moves by
+  2.5e-2 of max|O|).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_bound
+import oracle
+import workloads
+from gpu_util import host, note, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+L, H = 65536, 64
+HEADS = (0, 29, 63)
+CASES = {  # D: (Z, n_q, n_k); the live samples straddle 2^31 and 2^32 bytes
+    128: (5, [0, 65, 0, 2113, 3001], [0, 130, 0, 2987, 1999]),
+    64: (9, [0, 0, 0, 0, 0, 0, 0, 1500, 2600], [0, 0, 0, 0, 0, 0, 0, 2400, 1700]),
+}
+
+
+def _big_inputs(D, seed):
+    """Device q, k, v, do [Z, L, H, D] bf16 with seeded N(0,1) values on the live
+    rows, and those rows on the host (float64) per live sample."""
+    Z, nq, nk = CASES[D]
+    shape = (Z, L, H, D)
+    dev = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    live = {}
+    for z in range(Z):
+        a, b = nq[z], nk[z]
+        if a == 0 and b == 0:
+            continue
+        q, k, v, do = workloads.make_tensors(1, max(a, b), H, D, "bf16", seed=seed + z)
+        for t, src, n in zip(dev, (q, k, v, do), (a, b, b, a)):
+            t[z, :n] = src[0, :n].to("cuda")
+        live[z] = tuple(workloads.to_f64(t)[0] for t in (q, k, v, do))
+    torch.cuda.synchronize()
+    return dev, np.array(nq), np.array(nk), live
+
+
+def _assert_rest_zero(name, t, n):
+    """Every row of t at or past n[z] is exactly 0 (NaN counts as nonzero)."""
+    for z, nz in enumerate(n):
+        bad = int(torch.count_nonzero(t[z, int(nz):]))
+        assert bad == 0, f"{name}: {bad} nonzero elements in the padded rows of sample {z}"
+
+
+def _fp8_rows(qd, kd, alpha, bias, n, extra=96):
+    """Rows of one FP8 slice to check: the edges, random rows, and the 32 rows with
+    the largest single weight (where one key dominates a row, a code decided at a
+    rounding boundary moves O most)."""
+    rng = np.random.default_rng(n)
+    pmax = oracle.sigmoid(alpha * (qd @ kd.T) + bias).max(axis=1)
+    top = np.argsort(pmax)[::-1][:32].tolist()
+    fixed = [0, 1, 63, 64, 127, 128, n - 1]
+    return np.array(sorted({r for r in fixed + top + rng.integers(0, n, extra).tolist() if 0 <= r < n}))
+
+
+def _counters(sa, D, Z):
+    tcs = {}
+    for name, kern, axis in (("fwd", sa.KERNEL_FWD, 0), ("dq", sa.KERNEL_DQ, 0), ("dkdv", sa.KERNEL_DKDV, 1)):
+        bq, bk = sa.sigattn_tile_config(kern, D, torch.bfloat16)
+        tcs[name] = (bq, bk, torch.full((Z * H * -(-L // (bq if axis == 0 else bk)),), -7, dtype=torch.int32,
+                                         device="cuda"))
+    return tcs
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_sigmoid_past_4gib(D):
+    import padding_aware_sigmoid_amd as sa
+
+    Z, _, _ = CASES[D]
+    note(f"large sigmoid D={D} Z={Z} L={L} H={H} ({Z * L * H * D * 2 / 2**30:.1f} GiB per tensor)")
+    (q, k, v, do), nq, nk, live = _big_inputs(D, seed=90 + D)
+    alpha, bias = 1.0 / np.sqrt(D), -np.log(L)
+    tcs = _counters(sa, D, Z)
+    o = sa.sigattn_fwd(q, k, v, nq, nk, alpha, bias, tile_counts=tcs["fwd"][2])
+    dq, dk, dv = sa.sigattn_bwd(q, k, v, do, nq, nk, alpha, bias, tile_counts_dq=tcs["dq"][2],
+                                tile_counts_dkdv=tcs["dkdv"][2])
+    torch.cuda.synchronize()
+    for name, (bq, bk, t) in tcs.items():
+        by_q, by_k = oracle.tile_plan(nq, nk, L, bq, bk)
+        want = by_k if name == "dkdv" else by_q
+        got = t.cpu().numpy().reshape(Z, H, -1)
+        for h in range(H):
+            assert np.array_equal(got[:, h], want), f"{name}: tile counters differ from the plan (head {h})"
+    for name, t, n in (("O", o, nq), ("dQ", dq, nq), ("dK", dk, nk), ("dV", dv, nk)):
+        _assert_rest_zero(name, t, n)
+    for z, (Q, K, V, DO) in live.items():
+        a, b = int(nq[z]), int(nk[z])
+        for name, t, n in (("O", o, a), ("dQ", dq, a), ("dK", dk, b), ("dV", dv, b)):
+            assert bool(torch.isfinite(t[z, :n]).all()), f"{name}: non-finite value in sample {z}"
+        for h in HEADS:
+            ro = oracle.head_forward(Q[:a, h], K[:b, h], V[:b, h], alpha, bias)
+            rq, rk, rv = oracle.head_backward(Q[:a, h], K[:b, h], V[:b, h], DO[:a, h], alpha, bias)
+            for name, t, ref, n in (("O", o, ro, a), ("dQ", dq, rq, a), ("dK", dk, rk, b), ("dV", dv, rv, b)):
+                e = rel_err(host(t[z, :n, h]), ref)
+                assert e <= TOL, f"{name}: rel err {e:.3e} (sample {z}, head {h})"
+    del q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+def test_softmax_past_4gib():
+    import padding_aware_sigmoid_amd as sa
+
+    SM = oracle.softmax_attention
+    D = 128
+    Z, _, _ = CASES[D]
+    note(f"large softmax D={D} Z={Z} L={L} H={H}")
+    (q, k, v, do), nq, nk, live = _big_inputs(D, seed=95)
+    alpha = 1.0 / np.sqrt(D)
+    o, lse = sa.sigattn_softmax_fwd(q, k, v, nq, nk, alpha)
+    dq, dk, dv = sa.sigattn_softmax_bwd(q, k, v, o, do, lse, nq, nk, alpha)
+    torch.cuda.synchronize()
+    for name, t, n in (("O", o, nq), ("dQ", dq, nq), ("dK", dk, nk), ("dV", dv, nk)):
+        _assert_rest_zero(f"softmax {name}", t, n)
+    for z, (Q, K, V, DO) in live.items():
+        a, b = int(nq[z]), int(nk[z])
+        for h in HEADS:
+            ro, _ = SM.head_forward(Q[:a, h], K[:b, h], V[:b, h], alpha)
+            rq, rk, rv = SM.head_backward(Q[:a, h], K[:b, h], V[:b, h], DO[:a, h], alpha)
+            for name, t, ref, n in (("O", o, ro, a), ("dQ", dq, rq, a), ("dK", dk, rk, b), ("dV", dv, rv, b)):
+                e = rel_err(host(t[z, :n, h]), ref)
+                assert e <= TOL, f"softmax {name}: rel err {e:.3e} (sample {z}, head {h})"
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+def test_fp8_past_4gib():
+    """Codes are one byte, so the FP8 tensors reach 2.5 GiB and the bf16 O 5 GiB."""
+    import padding_aware_sigmoid_amd as sa
+
+    F8 = oracle.fp8_attention
+    D = 128
+    Z, _, _ = CASES[D]
+    note(f"large fp8 D={D} Z={Z} L={L} H={H}")
+    (q, k, v, _), nq, nk, live = _big_inputs(D, seed=97)
+    alpha, bias = 1.0 / np.sqrt(D), -np.log(L)
+    q8, sq = sa.sigattn_quantize_fp8(q, nq)
+    k8, sk = sa.sigattn_quantize_fp8(k, nk)
+    v8, sv = sa.sigattn_quantize_fp8(v, nk)
+    o = sa.sigattn_fwd_fp8(q8, k8, v8, sq, sk, sv, nq, nk, alpha, bias)
+    torch.cuda.synchronize()
+    _assert_rest_zero("fp8 O", o, nq)
+    for name, t, n in (("q8", q8, nq), ("k8", k8, nk), ("v8", v8, nk)):
+        _assert_rest_zero(name, t, n)
+    for name, s, n in (("sq", sq, nq), ("sk", sk, nk), ("sv", sv, nk)):
+        sh = s.cpu().numpy()
+        for z in range(Z):
+            live_tiles = -(-int(n[z]) // F8.TILE)
+            assert np.all(sh[z, :, live_tiles:] == 127), f"{name}: scale of a tile past n is not 2^0 (sample {z})"
+    for z, (Q, K, V, _) in live.items():
+        a, b = int(nq[z]), int(nk[z])
+        for h in HEADS:
+            codes, exps = {}, {}
+            for name, x, c8, s, n in (("q8", Q, q8, sq, a), ("k8", K, k8, sk, b), ("v8", V, v8, sv, b)):
+                rc, rs = F8.quantize(x[None, :n, h:h + 1], [n])
+                gc = c8[z, :n, h].cpu().numpy()
+                gs = s[z, h, :rs.shape[2]].cpu().numpy()
+                assert np.array_equal(gc, rc[0, :, 0]), f"{name}: codes differ (sample {z}, head {h})"
+                assert np.array_equal(gs, rs[0, 0]), f"{name}: scale bytes differ (sample {z}, head {h})"
+                codes[name] = F8.dequantize(rc, rs)[0, :, 0]
+                exps[name] = fp8_bound.row_exps(rs[0, 0], n)
+            rows = _fp8_rows(codes["q8"], codes["k8"], alpha, bias, a)
+            r = fp8_bound.check_slice(host(o[z, torch.as_tensor(rows, device="cuda"), h]), codes["q8"], codes["k8"],
+                                      codes["v8"], alpha, bias, exps["q8"], exps["k8"], exps["v8"],
+                                      f"fp8 O (sample {z}, head {h})", rows=rows)
+            note(f"  fp8 sample {z} head {h}: rel err vs oracle {r['oracle']:.2e}, vs MFMA-formed {r['hw']:.2e} "
+                 f"(bound use {r['hw_ratio']:.3f}), vs exact (bound use {r['exact_ratio']:.3f})")
+    del q, k, v, q8, k8, v8, o
+    torch.cuda.empty_cache()

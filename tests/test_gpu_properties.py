@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import device_inputs, host, note
+from gpu_util import device_inputs, note
 
 pytestmark = pytest.mark.gpu
 
