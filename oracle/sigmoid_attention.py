@@ -28,7 +28,7 @@ Models" (arXiv:2604.27124):
   (paperlayer.ai summary, section 1). The packed (varlen) layout used by
   forward_varlen and backward_varlen stores the samples' valid rows back to
   back, with cumulative offsets, in place of padding. That storage variant is
-  this build's own; the pages do not describe it. Attention stays per sample,
+  this library's own; the pages do not describe it. Attention stays per sample,
   so the results are those of the padded layout on the same valid rows.
 
 Readings taken where the pages are silent (each is listed in the design notes):
