@@ -13,7 +13,7 @@ summary, section 5) and give no scheme. The forward computed here is the
 sigmoid forward of the rest of the oracle (gist.science summary, section 2.A;
 rainbus.top summary, "方法步骤详情", steps 1-3) on quantised operands.
 
-Readings taken where the pages are silent (listed in the design notes):
+Readings taken where the pages are silent:
 
 * Format: OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7,
   3 mantissa bits, subnormals with step 2^-9, largest finite value 448, no

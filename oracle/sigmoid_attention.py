@@ -31,7 +31,7 @@ Models" (arXiv:2604.27124):
   this library's own; the pages do not describe it. Attention stays per sample,
   so the results are those of the padded layout on the same valid rows.
 
-Readings taken where the pages are silent (each is listed in the design notes):
+Readings taken where the pages are silent:
 
 * A key j >= n_k gets weight exactly 0. The -inf score is read as a select,
   not an addition.

@@ -19,7 +19,7 @@ for single-cell Foundation Models", arXiv:2604.27124):
   sigmoid oracle: only keys j < n_k[z] take part, query rows i >= n_q[z] are
   outputs defined as 0, and padded inputs are never read.
 
-Readings taken where the pages are silent (listed in the design notes):
+Readings taken where the pages are silent:
 
 * A score bias b adds the same constant to a whole row, which softmax removes,
   so the softmax path has no bias argument.
