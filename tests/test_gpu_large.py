@@ -192,3 +192,53 @@ def test_fp8_past_4gib():
                  f"(bound use {r['hw_ratio']:.3f}), vs exact (bound use {r['exact_ratio']:.3f})")
     del q, k, v, q8, k8, v8, o
     torch.cuda.empty_cache()
+
+
+def test_max_length():
+    """L = 262144, the FP8 forward's limit (4096 key-tile scale bytes in LDS),
+    every key live (n_k = L) and a short query side, D = 64: the bf16 path in
+    full against the oracle, the FP8 codes bit for bit and the FP8 forward
+    against both references of tests/fp8_bound.py on sampled rows (the bound
+    against exact attention on every row)."""
+    import padding_aware_sigmoid_amd as sa
+
+    F8 = oracle.fp8_attention
+    Z, Lm, Hm, D = 1, 262144, 2, 64
+    nq, nk = np.array([130]), np.array([Lm])
+    note(f"max length Z={Z} L={Lm} H={Hm} D={D} n_q={nq[0]} n_k={nk[0]}")
+    q, k, v, do = workloads.make_tensors(Z, Lm, Hm, D, "bf16", seed=99)
+    dq_, dk_, dv_, ddo = (t.to("cuda") for t in (q, k, v, do))
+    alpha, bias = 1.0 / np.sqrt(D), -np.log(Lm)
+    o = sa.sigattn_fwd(dq_, dk_, dv_, nq, nk, alpha, bias)
+    gq, gk, gv = sa.sigattn_bwd(dq_, dk_, dv_, ddo, nq, nk, alpha, bias)
+    q8, sq = sa.sigattn_quantize_fp8(dq_, nq)
+    k8, sk = sa.sigattn_quantize_fp8(dk_, nk)
+    v8, sv = sa.sigattn_quantize_fp8(dv_, nk)
+    o8 = sa.sigattn_fwd_fp8(q8, k8, v8, sq, sk, sv, nq, nk, alpha, bias)
+    torch.cuda.synchronize()
+    for name, t, n in (("O", o, nq), ("dQ", gq, nq), ("dK", gk, nk), ("dV", gv, nk), ("fp8 O", o8, nq)):
+        _assert_rest_zero(name, t, n)
+    Q, K, V, DO = (workloads.to_f64(t)[0] for t in (q, k, v, do))
+    a = int(nq[0])
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, 129} | set(np.random.default_rng(1).integers(0, a, 9).tolist())))
+    for h in range(Hm):
+        ro = oracle.head_forward(Q[:a, h], K[:, h], V[:, h], alpha, bias)
+        rq, rk, rv = oracle.head_backward(Q[:a, h], K[:, h], V[:, h], DO[:a, h], alpha, bias)
+        for name, t, ref, n in (("O", o, ro, a), ("dQ", gq, rq, a), ("dK", gk, rk, Lm), ("dV", gv, rv, Lm)):
+            e = rel_err(host(t[0, :n, h]), ref)
+            assert e <= TOL, f"{name}: rel err {e:.3e} (head {h})"
+        codes, exps = {}, {}
+        for name, x, c8, s, n in (("q8", Q, q8, sq, a), ("k8", K, k8, sk, Lm), ("v8", V, v8, sv, Lm)):
+            rc, rs = F8.quantize(x[None, :n, h:h + 1], [n])
+            assert np.array_equal(c8[0, :n, h].cpu().numpy(), rc[0, :, 0]), f"{name}: codes differ (head {h})"
+            assert np.array_equal(s[0, h, :rs.shape[2]].cpu().numpy(), rs[0, 0]), f"{name}: scales differ (head {h})"
+            codes[name] = F8.dequantize(rc, rs)[0, :, 0]
+            exps[name] = fp8_bound.row_exps(rs[0, 0], n)
+        x = (exps["q8"], exps["k8"], exps["v8"])
+        hw, hb, _ = fp8_bound.hw_forward(codes["q8"], codes["k8"], codes["v8"], alpha, bias, *x, rows=rows)
+        g8 = host(o8[0, :a, h])
+        fp8_bound.check(g8[rows], hw, hb, f"fp8 O (head {h}) vs the MFMA-formed forward")
+        ex, eb = fp8_bound.exact_bound(codes["q8"], codes["k8"], codes["v8"], alpha, bias, *x)
+        fp8_bound.check(g8, ex, eb, f"fp8 O (head {h}) vs exact attention")
+    del dq_, dk_, dv_, ddo, o, gq, gk, gv, q8, k8, v8, o8
+    torch.cuda.empty_cache()
