@@ -51,32 +51,6 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return z;
 }
 
-// Transposed LDS read feeding the B operand of mfma32 from a row-major tile
-// T[row][col] (bf16, `ld` elements per row) whose rows are the contraction
-// index.
-//
-// ds_read_b64_tr_b16 works per group of 16 lanes (measured on gfx950). Lane i
-// of a group receives, for j = 0..3, element i%4 of the 8-byte chunk that lane
-// 4j + i/4 of the same group addresses.
-//
-// The result: lane l receives T[row0 + 8*part + 4*(l/32) + j][col0 + l%32] for
-// j = 0..3, where part 0 and part 1 are the two reads. That is the row order
-// described above for k-step rows row0..row0+15.
-__device__ __forceinline__ bf16x8 lds_read_b_tr(const __bf16* tile, int ld, int row0, int col0, int lane) {
-  const int g = lane >> 4;  // 16-lane group
-  const int s = lane & 15;
-  const int row = row0 + 4 * (g >> 1) + (s >> 2);
-  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
-  const __bf16* p0 = tile + row * ld + col;
-  const __bf16* p1 = p0 + 8 * ld;
-  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
-  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
 // Scheduling hint for one region of the key loop: N groups of one MFMA
 // followed by up to V VALU instructions. The MFMA pipe then runs beside the
 // sigma work instead of in separate bursts. (Mask bits: 0x008 MFMA,
