@@ -175,3 +175,46 @@ def test_split_backward_entry_points_match(dtype, D):
     assert torch.equal(a[0], gq) and torch.equal(a[1], gk) and torch.equal(a[2], gv)
     assert torch.equal(a[1], hk) and torch.equal(a[2], hv)
     assert torch.equal(c0, c1) and torch.equal(c0, c2) and int(c0.min()) >= 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("bias_mode", ["constant", "neg_log_nk"])
+def test_autograd_matches_entry_points_and_oracle(dtype, bias_mode):
+    """sigmoid_attention (the autograd wrapper over the padded layout): its
+    forward and its gradients equal sigattn_fwd / sigattn_bwd bit for bit,
+    with the default alpha = 1/sqrt(D) and bias (-ln L for one bias; b_z =
+    -ln n_k[z] per sample), and both match the oracle."""
+    import padding_aware_sigmoid_amd as sa
+
+    from gpu_util import host, rel_err
+
+    Z, L, H, D = 3, 200, 2, 64
+    n = np.array([200, 77, 0])
+    note(f"padded autograd {dtype} {bias_mode}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, dtype, seed=31)
+    dq_, dk_, dv_, ddo, dn, _ = device_inputs(q, k, v, do, n, n)
+    leaves = [t.clone().requires_grad_(True) for t in (dq_, dk_, dv_)]
+    o = sa.sigmoid_attention(*leaves, dn, dn, bias_mode=bias_mode)
+    o.backward(ddo)
+    # the wrapper's defaults: bias = -ln L for one bias, 0 (so b_z = -ln n_k[z]) per sample
+    alpha, bias = 1 / math.sqrt(D), (-math.log(L) if bias_mode == "constant" else 0.0)
+    o2 = sa.sigattn_fwd(dq_, dk_, dv_, dn, dn, alpha, bias, bias_mode=bias_mode)
+    g2 = sa.sigattn_bwd(dq_, dk_, dv_, ddo, dn, dn, alpha, bias, bias_mode=bias_mode)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    for leaf, g in zip(leaves, g2):
+        assert torch.equal(leaf.grad, g)
+    Q, K, V, DO = (workloads.to_f64(t) for t in (q, k, v, do))
+    if bias_mode == "constant":
+        ref_o = oracle.forward(Q, K, V, n, n, alpha, bias)
+        ref_g = oracle.backward(Q, K, V, DO, n, n, alpha, bias)
+    else:
+        b = oracle.per_sample_bias(n, bias)
+        ref_o = oracle.forward(Q, K, V, n, n, alpha, b)
+        ref_g = oracle.backward(Q, K, V, DO, n, n, alpha, b)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for name, got, ref in zip(("O", "dQ", "dK", "dV"), (o2, *g2), (ref_o, *ref_g)):
+        g = host(got)
+        err = rel_err(g, ref)
+        assert err <= tol, f"{name}: {err:.3e} > {tol}"
+        assert np.all(g[1, 77:] == 0.0) and np.all(g[2] == 0.0), f"{name}: padded rows not 0"
