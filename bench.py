@@ -58,7 +58,7 @@ def parse():
                     help="workload of the FP8 forward sub-object ('' to skip)")
     ap.add_argument("--softmax-workload", default="nopad16k",
                     help="workload of the softmax fwd+bwd sub-object ('' to skip)")
-    ap.add_argument("--configs", default="tiny,nopad16k,pad25_16k,cellbatch8k,stress8k@1,stress8k@4,stress8k@16",
+    ap.add_argument("--configs", default="tiny,nopad16k,pad25_16k,cellbatch8k,nopad8k_d64,stress8k@1,stress8k@4,stress8k@16",
                     help="workloads (name or name@qk_scale) whose per-pass TFLOP/s the line reports under 'configs' "
                          "('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -425,6 +425,7 @@ def main():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     import padding_aware_sigmoid_amd as sa
+    import workloads
 
     sa.load()
     main_res = run_gpu(args.workload, args.steps, args.warmup)
@@ -482,6 +483,17 @@ def main():
         }
     if args.varlen_workload not in ("", "none"):
         line["varlen"] = run_layouts(args.varlen_workload, args.steps, args.warmup)
+        # the same shape with no padding, when the config sweep timed it: how
+        # close the cell batch comes to its kernels' rate on full tiles
+        vw = workloads.WORKLOADS[args.varlen_workload]
+        for key, rec in configs.items():
+            cw = workloads.WORKLOADS[key.partition("@")[0]]
+            if (cw.length_model == "full" and (cw.Z, cw.H, cw.L, cw.D) == (vw.Z, vw.H, vw.L, vw.D)
+                    and rec.get("tflops_valid")):
+                line["varlen"]["nopad_same_shape"] = {
+                    "workload": key, "tflops_valid": rec["tflops_valid"],
+                    "padded_frac_of_nopad": round(line["varlen"]["padded_tflops_valid"] / rec["tflops_valid"], 4),
+                    "packed_frac_of_nopad": round(line["varlen"]["packed_tflops_valid"] / rec["tflops_valid"], 4)}
     if args.fp8_workload not in ("", "none"):
         line["fp8"] = run_fp8(args.fp8_workload, args.steps, args.warmup)
     if args.softmax_workload not in ("", "none"):

@@ -16,6 +16,8 @@ Shapes and length mixes follow the pages' workloads:
   2048/4096/8192/16384 genes). They are padded to L=8192 with D=64, the head
   size of the 160M model (768 hidden / 12 heads, rainbus.top reproduction
   notes).
+* "nopad8k_d64": the cell batch's shape (Z=16, H=12, L=8192, D=64) with no
+  padding, the rate its kernels reach when every tile is full.
 * "stress8k": L=8192, D=64 with Q and K scaled up to produce large scores,
   standing in for the 8K no-clipping stress test (paperlayer.ai summary,
   section 5).
@@ -72,6 +74,9 @@ WORKLOADS = {
                           description="kernel bench, L=16K, D=128, 25% of tokens padding"),
     "cellbatch8k": Workload("cellbatch8k", 16, 12, 8192, 64, "bf16", "lognormal_cells",
                             description="cell batch, log-normal gene counts clipped to 8192"),
+    "nopad8k_d64": Workload("nopad8k_d64", 16, 12, 8192, 64, "bf16", "full",
+                            description="the cell batch's shape with every sample at L: its kernels' rate "
+                                        "without padding"),
     "stress8k": Workload("stress8k", 8, 12, 8192, 64, "bf16", "uniform_1k_8k", qk_scales=(1.0, 4.0, 16.0),
                          description="long-context stress, Q,K ~ N(0, s^2)"),
 }
