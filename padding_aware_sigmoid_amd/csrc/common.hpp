@@ -44,6 +44,46 @@ __device__ __forceinline__ float sigmoid_dot(float s, float c1, float c0) {
   return __builtin_amdgcn_rcpf(1.0f + t);
 }
 
+// sigma with one transcendental, for scores far below 0. With t = e^S =
+// 2^(-c1*s - c0), sigma(S) = t / (1 + t) = t - t^2 + t^3 / (1 + t), so t - t^2
+// (one FMA) has relative error t^2 / (1 + t) < t^2: below 2^-10, a quarter of
+// P's bf16 rounding step, while t <= 2^-5 (S <= -3.47). The bias b = -ln n of
+// the method puts nearly every score there (S ~ b + N(0, 1) for unit-variance
+// inputs, b = -9 at n = 8192). The caller keeps the bit pattern of the
+// largest t in tmax (t >= 0, so unsigned order is float order, and a NaN t
+// compares above the bound) and recomputes with sigmoid_dot every weight of
+// a block in which some lane's tmax exceeds kSmallSigmaMaxBits.
+constexpr uint32_t kSmallSigmaMaxBits = 0x3D000000u;  // bits of 2^-5
+
+__device__ __forceinline__ float sigmoid_dot_small(float s, float c1, float c0, uint32_t& tmax) {
+  const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(s, -c1, -c0));
+  tmax = max(tmax, __float_as_uint(t));
+  return __builtin_fmaf(-t, t, t);
+}
+
+// One of the two, chosen at compile time.
+template <bool SMALL>
+__device__ __forceinline__ float sigmoid_pass(float s, float c1, float c0, uint32_t& tmax) {
+  if constexpr (SMALL) return sigmoid_dot_small(s, c1, c0, tmax);
+  else return sigmoid_dot(s, c1, c0);
+}
+
+// Whether some lane of the wave saw a t above the bound (a wave-uniform value).
+__device__ __forceinline__ bool small_sigma_out_of_range(uint32_t tmax) {
+  return __builtin_amdgcn_ballot_w64(tmax > kSmallSigmaMaxBits) != 0;
+}
+
+// A launch uses sigmoid_dot_small when c0 = -b log2(e) of its samples is at
+// least this: then a score of 0 (as a zero-filled padded key row gets) has
+// t = 2^-c0 <= 2^-6, inside the range, and typical scores are far inside it.
+// For a per-sample bias b_z = bias - ln n_k[z] the test takes n_k = L / 2.
+// Below it nearly every block would need the recomputation.
+constexpr float kSmallSigmaMinC0 = 6.0f;
+
+__host__ __device__ inline bool use_small_sigma(float c0, int L, int bias_per_sample) {
+  return (bias_per_sample ? c0 + __builtin_log2f((float)(L > 2 ? L : 2)) - 1.0f : c0) >= kSmallSigmaMinC0;
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
 #pragma unroll

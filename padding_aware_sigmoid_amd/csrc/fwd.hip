@@ -22,7 +22,11 @@
 //  - Scores are computed transposed, S^T = K Q^T, so the accumulator already
 //    has the layout of the A operand of P V. P never leaves registers.
 //  - V reaches the MFMA through ds_read_b64_tr_b16.
-//  - sigma takes one v_exp_f32 and one v_rcp_f32 per score.
+//  - sigma takes one v_exp_f32 and one FMA per score, t - t^2 with t = e^S,
+//    on every 32 x 32 block of weights whose scores all lie at or below -3.47
+//    (relative error under 2^-10; the bias b = -ln n puts nearly all scores
+//    there), and the exact 1 / (1 + e^-S) (v_exp_f32, v_rcp_f32) on the
+//    others: a ballot after each block tells the wave to recompute it.
 #include "common.hpp"
 
 namespace sigattn {
@@ -69,6 +73,13 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], 
     }
 }
 
+// P for the wave's two 32-query blocks and one 32-key block, with the exact
+// sigma (the fallback of the one-transcendental form).
+__device__ __forceinline__ void sigmoid_exact_block(bf16x8 (&p)[2][2], const f32x16 (&s)[2], float c1, float c0) {
+#pragma unroll
+  for (int e = 0; e < 32; ++e) p[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_dot(s[e >> 4][e & 15], c1, c0);
+}
+
 // The forward of one wave, written as a fixed step schedule. With one wave per
 // SIMD, latency can only be hidden inside the wave's own instruction stream.
 // Key tile t is two phases of NSTEP steps, 2 MFMAs each:
@@ -89,12 +100,13 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[2][FwdCfg<D>::NB], 
 // (2 * NSTEP is a multiple of 4).
 // Slots: kT, vT hold tile t; vP holds tile t-1 (phase A's P V); kN holds tile
 // t+1 (phase B's S, and the reads ahead into the next phase A).
-template <int D, int G0, int G1, typename AtBarrier, typename DmaChunk>
+template <int D, int G0, int G1, bool SMALL, typename AtBarrier, typename DmaChunk>
 __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, const __bf16* vT, const __bf16* kN,
                                           f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                           f32x16 (&oacc)[2][FwdCfg<D>::NB], bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
                                           bf16x8 (&ops)[4], const bf16x8 (&qf)[2][FwdCfg<D>::KS], float c1, float c0,
-                                          int l32, int half, int lane, AtBarrier&& at_barrier, DmaChunk&& dma_chunk) {
+                                          uint32_t& tmax, int l32, int half, int lane, AtBarrier&& at_barrier,
+                                          DmaChunk&& dma_chunk) {
   using C = FwdCfg<D>;
   constexpr int KS = C::KS, NB2 = 2 * C::NB;
   constexpr int NSTEP = KS + NB2;  // steps per phase: 16 at D = 128, 8 at D = 64
@@ -136,6 +148,13 @@ __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, co
     if constexpr (g == NSTEP) {
       pin_before_barrier(p0);
       at_barrier();
+      // With the one-transcendental sigma: P(t, 1st half) is complete here and
+      // unused so far, and its scores are intact until the next line. If one
+      // of them left the form's range, the wave recomputes the block exactly.
+      if constexpr (SMALL) {
+        if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p0, s_cur, c1, c0);
+        tmax = 0;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_cur[0][r] = s_cur[1][r] = 0.0f;
     }
@@ -164,10 +183,16 @@ __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, co
     static_for<e0, e1>([&](auto ec) {
       constexpr int e = decltype(ec)::value, qb = e >> 4, r = e & 15;
       if constexpr (g < NSTEP)
-        p0[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_cur[qb][r], c1, c0);
+        p0[qb][r >> 3][r & 7] = (__bf16)sigmoid_pass<SMALL>(s_cur[qb][r], c1, c0, tmax);
       else
-        p1[qb][r >> 3][r & 7] = (__bf16)sigmoid_dot(s_nxt[qb][r], c1, c0);
+        p1[qb][r >> 3][r & 7] = (__bf16)sigmoid_pass<SMALL>(s_nxt[qb][r], c1, c0, tmax);
     });
+    // P(t, 2nd half) is complete at the last step of phase B, and its scores
+    // are intact until the next phase starts: the same check and recomputation.
+    if constexpr (SMALL && g == G - 1) {
+      if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p1, s_nxt, c1, c0);
+      tmax = 0;
+    }
     constexpr bool dma_here = g >= NSTEP && (g - NSTEP) % DSTRIDE == 0 && (g - NSTEP) / DSTRIDE < NDMA;
     if constexpr (dma_here) {
       dma_chunk((g - NSTEP) / DSTRIDE);
@@ -177,7 +202,7 @@ __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, co
     // now that every LDS operand address is a base register plus an
     // immediate: without them 1.91 -> 1.82 ms (nopad16k). At D = 64 they
     // stay (within 1% either way).
-    if constexpr (D != 128) sched_step<g, reads_of(g + 3), 2, 5 * (e1 - e0), 2>();
+    if constexpr (D != 128) sched_step<g, reads_of(g + 3), 2, (SMALL ? 4 : 5) * (e1 - e0), 2>();
   });
 }
 
@@ -195,7 +220,7 @@ __device__ __forceinline__ void fwd_steps(const __bf16* kT, const __bf16* vP, co
 // tile 0's scores, each loop body one more tile, and the epilogue finishes the
 // last tile's P V. Tile t sits in slot t mod 3. tile_counts receives the
 // number of key tiles whose scores this workgroup computed.
-template <int D>
+template <int D, bool SMALL>
 __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                        SeqLayout sl, int Z, int H, float c1, float c0_base,
@@ -270,11 +295,13 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
 
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 p0[2][2], p1[2][2], ops[4];
+    uint32_t tmax = 0;  // the largest t = e^S of the current half-tile (SMALL)
     // Prologue: S(0, 1st half), then S(0, 2nd half) beside P(0, 1st half) = sigma(S).
     scores_t<D>(s_cur, sK0, 0, qf, l32, half);
     scores_t<D>(s_nxt, sK0, 1, qf, l32, half);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) p0[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_dot(s_cur[e >> 4][e & 15], c1, c0);
+    for (int e = 0; e < 32; ++e)
+      p0[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SMALL>(s_cur[e >> 4][e & 15], c1, c0, tmax);
     interleave_mfma_valu<2 * C::KS, 10>();
     // the operands of phase B's first three steps: V of tile 0, 1st half
 #pragma unroll
@@ -304,12 +331,12 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
       };
       auto none = [](int) {};
       auto no_barrier = [] {};
-      fwd_steps<D, NSTEP, G>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
-                             ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
-                             at_barrier, dma_chunk);
-      fwd_steps<D, 0, NSTEP>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
-                             ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, l32, half, lane,
-                             no_barrier, none);
+      fwd_steps<D, NSTEP, G, SMALL>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
+                                    ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
+                                    half, lane, at_barrier, dma_chunk);
+      fwd_steps<D, 0, NSTEP, SMALL>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
+                                    ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
+                                    half, lane, no_barrier, none);
       ++executed;
     };
     using I0 = std::integral_constant<int, 0>;
@@ -332,10 +359,19 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
     // P(2nd half) = sigma(S), then P(2nd half) V.
     const int last = nb - nb3;
     const __bf16* vL = last == 0 ? sV0 : (last == 1 ? sV1 : sV2);
+    // P(last, 1st half) meets no barrier before its use: the check here.
+    if constexpr (SMALL) {
+      if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p0, s_cur, c1, c0);
+      tmax = 0;
+    }
     accumulate_pv<D>(oacc, p0, vL, 0, lane);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) p1[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_dot(s_nxt[e >> 4][e & 15], c1, c0);
+    for (int e = 0; e < 32; ++e)
+      p1[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SMALL>(s_nxt[e >> 4][e & 15], c1, c0, tmax);
     interleave_mfma_valu<2 * C::NB * 2, 10>();
+    if constexpr (SMALL) {
+      if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p1, s_nxt, c1, c0);
+    }
     accumulate_pv<D>(oacc, p1, vL, 1, lane);
     dma_wait();  // the last body's DMA (all zeros) must not outlive the kernel
   }
@@ -419,8 +455,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            float c1, float c0, int32_t* tc, hipStream_t st) {
   using C = FwdCfg<D>;
   const long long blocks = (long long)Z * H * ((sl.L + C::BQ - 1) / C::BQ);
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, sl, Z, H, c1, c0, tc);
+  if (use_small_sigma(c0, sl.L, sl.bias_per_sample))
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, sl, Z, H, c1, c0, tc);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, sl, Z, H, c1, c0, tc);
   return hipGetLastError();
 }
 
