@@ -26,7 +26,9 @@
 //    on every 32 x 32 block of weights whose scores all lie at or below -3.47
 //    (relative error under 2^-10; the bias b = -ln n puts nearly all scores
 //    there), and the exact 1 / (1 + e^-S) (v_exp_f32, v_rcp_f32) on the
-//    others: a ballot after each block tells the wave to recompute it.
+//    others: a ballot after each block tells the wave to recompute it. A
+//    workgroup whose first block of scores already leaves that range (large
+//    score norms) runs the exact form throughout.
 #include "common.hpp"
 
 namespace sigattn {
@@ -235,6 +237,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
   __shared__ __attribute__((aligned(1024))) __bf16 sV2[C::TILE];
 
   __shared__ RankLds rank_lds;
+  __shared__ int vote;  // a wave's first block left the one-transcendental range
   const int n_qt = (sl.L + C::BQ - 1) / C::BQ;
   const TileCoord tc = schedule_tile(blockIdx.x, Z, H, n_qt, sl, rank_lds);
   const int z = tc.z, h = tc.h, m = tc.m;
@@ -287,93 +290,128 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
       dma_tile<D, C::BK, 256>(sk, Kb + off, row_bytes, nk - k0, tid);
       dma_tile<D, C::BK, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
-    // Tile t sits in slot t mod 3.
-    fetch(sK0, sV0, 0);
-    if (nkt > 1) fetch(sK1, sV1, 1);
-    dma_wait();
-    __syncthreads();
-
-    f32x16 s_cur[2], s_nxt[2];
-    bf16x8 p0[2][2], p1[2][2], ops[4];
-    uint32_t tmax = 0;  // the largest t = e^S of the current half-tile (SMALL)
-    // Prologue: S(0, 1st half), then S(0, 2nd half) beside P(0, 1st half) = sigma(S).
-    scores_t<D>(s_cur, sK0, 0, qf, l32, half);
-    scores_t<D>(s_nxt, sK0, 1, qf, l32, half);
+    // A launch allowed the one-transcendental form (SMALL) takes it in a
+    // workgroup only if every wave's first 32 x 32 block of scores lies well
+    // inside the form's range (t <= 2^-6), tested on K tile 0 before the key
+    // loop. Inputs whose scores leave the range (large norms) show it at
+    // once, and the workgroup then runs the exact form throughout instead of
+    // computing most blocks twice. Either way each block is checked before
+    // use. The decision is the workgroup's (a vote in LDS), so all waves run
+    // the same loop.
+    bool small_wg = false;
+    if constexpr (SMALL) {
+      if (tid == 0) vote = 0;
+      dma_tile<D, C::BK, 256>(sK0, Kb, row_bytes, nk, tid);
+      dma_wait();
+      __syncthreads();
+      f32x16 probe[2];
+      scores_t<D>(probe, sK0, 0, qf, l32, half);
+      float ymax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; ++e)
-      p0[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SMALL>(s_cur[e >> 4][e & 15], c1, c0, tmax);
-    interleave_mfma_valu<2 * C::KS, 10>();
-    // the operands of phase B's first three steps: V of tile 0, 1st half
-#pragma unroll
-    for (int i = 0; i < 3; ++i) ops[(2 * C::KS + 2 * C::NB + i) % 4] = lds_tr<D>(sV0, (i & 1) * 16, (i >> 1) * 32, lane);
-    executed = 1;
+      for (int e = 0; e < 32; ++e) ymax = fmaxf(ymax, __builtin_fmaf(probe[e >> 4][e & 15], -c1, -c0));
+      if (!(ymax <= -6.0f)) vote = 1;
+      __syncthreads();
+      small_wg = __builtin_amdgcn_readfirstlane(vote) == 0;
+    }
+    // The key loop, with one form of sigma or the other.
+    auto run = [&](auto sm_c) {
+      constexpr bool SM = decltype(sm_c)::value;
+      // Tile t sits in slot t mod 3. (Tile 0's K may be in slot 0 already,
+      // read by the test above before the last barrier; it is written again
+      // with the same bytes.)
+      fetch(sK0, sV0, 0);
+      if (nkt > 1) fetch(sK1, sV1, 1);
+      dma_wait();
+      __syncthreads();
 
-    // Loop body for tile t in slot T (tile t-1 in slot P, tile t+1 in slot N):
-    // phase B of tile t, then phase A of tile t+1. Phase B starts tile t+2's
-    // DMA into slot P (every wave has finished with tile t-1 at the barrier).
-    // The DMA of a tile past n_k (t + 2 = nkt) has no row in range and fills
-    // its slot with zeros, which nothing reads.
-    auto body = [&](auto t_c, auto p_c, auto n_c, int t) {
-      constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
-      constexpr int KS = C::KS, NSTEP = KS + 2 * C::NB, G = 2 * NSTEP;
-      auto dma_chunk = [&](int i) {
-        constexpr int NC = kDmaChunks<D, C::BK, 256>;
-        const int k0 = (t + 2) * C::BK;
-        const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
-        if (i < NC)
-          dma_tile_chunk<D, C::BK, 256>(ring<P>(sK0, sK1, sK2), Kb + off, row_bytes, nk - k0, tid, i);
-        else
-          dma_tile_chunk<D, C::BK, 256>(ring<P>(sV0, sV1, sV2), Vb + off, row_bytes, nk - k0, tid, i - NC);
+      f32x16 s_cur[2], s_nxt[2];
+      bf16x8 p0[2][2], p1[2][2], ops[4];
+      uint32_t tmax = 0;  // the largest t = e^S of the current half-tile (one-transcendental form)
+      // Prologue: S(0, 1st half), then S(0, 2nd half) beside P(0, 1st half) = sigma(S).
+      scores_t<D>(s_cur, sK0, 0, qf, l32, half);
+      scores_t<D>(s_nxt, sK0, 1, qf, l32, half);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        p0[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SM>(s_cur[e >> 4][e & 15], c1, c0, tmax);
+      interleave_mfma_valu<2 * C::KS, 10>();
+      // the operands of phase B's first three steps: V of tile 0, 1st half
+#pragma unroll
+      for (int i = 0; i < 3; ++i) ops[(2 * C::KS + 2 * C::NB + i) % 4] = lds_tr<D>(sV0, (i & 1) * 16, (i >> 1) * 32, lane);
+      executed = 1;
+
+      // Loop body for tile t in slot T (tile t-1 in slot P, tile t+1 in slot N):
+      // phase B of tile t, then phase A of tile t+1. Phase B starts tile t+2's
+      // DMA into slot P (every wave has finished with tile t-1 at the barrier).
+      // The DMA of a tile past n_k (t + 2 = nkt) has no row in range and fills
+      // its slot with zeros, which nothing reads.
+      auto body = [&](auto t_c, auto p_c, auto n_c, int t) {
+        constexpr int T = decltype(t_c)::value, P = decltype(p_c)::value, N = decltype(n_c)::value;
+        constexpr int KS = C::KS, NSTEP = KS + 2 * C::NB, G = 2 * NSTEP;
+        auto dma_chunk = [&](int i) {
+          constexpr int NC = kDmaChunks<D, C::BK, 256>;
+          const int k0 = (t + 2) * C::BK;
+          const size_t off = (size_t)(k0 < nk ? k0 : 0) * rs;  // no row is read past n_k
+          if (i < NC)
+            dma_tile_chunk<D, C::BK, 256>(ring<P>(sK0, sK1, sK2), Kb + off, row_bytes, nk - k0, tid, i);
+          else
+            dma_tile_chunk<D, C::BK, 256>(ring<P>(sV0, sV1, sV2), Vb + off, row_bytes, nk - k0, tid, i - NC);
+        };
+        auto at_barrier = [&] {
+          dma_wait();       // this wave's DMA of tile t+1 has landed
+          __syncthreads();  // ... everyone's has, and every wave is done with slot P
+        };
+        auto none = [](int) {};
+        auto no_barrier = [] {};
+        fwd_steps<D, NSTEP, G, SM>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
+                                      ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
+                                      half, lane, at_barrier, dma_chunk);
+        fwd_steps<D, 0, NSTEP, SM>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
+                                      ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
+                                      half, lane, no_barrier, none);
+        ++executed;
       };
-      auto at_barrier = [&] {
-        dma_wait();       // this wave's DMA of tile t+1 has landed
-        __syncthreads();  // ... everyone's has, and every wave is done with slot P
-      };
-      auto none = [](int) {};
-      auto no_barrier = [] {};
-      fwd_steps<D, NSTEP, G, SMALL>(ring<T>(sK0, sK1, sK2), ring<P>(sV0, sV1, sV2), ring<T>(sV0, sV1, sV2),
-                                    ring<N>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
-                                    half, lane, at_barrier, dma_chunk);
-      fwd_steps<D, 0, NSTEP, SMALL>(ring<N>(sK0, sK1, sK2), ring<T>(sV0, sV1, sV2), ring<N>(sV0, sV1, sV2),
-                                    ring<P>(sK0, sK1, sK2), s_cur, s_nxt, oacc, p0, p1, ops, qf, c1, c0, tmax, l32,
-                                    half, lane, no_barrier, none);
-      ++executed;
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      // Bodies for tiles 0 .. nkt-2: whole rounds of three (slots 0, 1, 2), then
+      // the one or two left over. The compiler keeps the three-body loop as free
+      // of spills as the earlier form (a loop entered or left in the middle of a
+      // round spilled up to 388 registers); the leftover bodies and the epilogue
+      // sit after it.
+      const int nb = nkt - 1, nb3 = nb / 3 * 3;
+      for (int t = 0; t < nb3; t += 3) {
+        body(I0{}, I2{}, I1{}, t);
+        body(I1{}, I0{}, I2{}, t + 1);
+        body(I2{}, I1{}, I0{}, t + 2);
+      }
+      if (nb3 < nb) body(I0{}, I2{}, I1{}, nb3);
+      if (nb3 + 1 < nb) body(I1{}, I0{}, I2{}, nb3 + 1);
+      // Epilogue, the last tile (slot nb mod 3): P(1st half) V beside
+      // P(2nd half) = sigma(S), then P(2nd half) V.
+      const int last = nb - nb3;
+      const __bf16* vL = last == 0 ? sV0 : (last == 1 ? sV1 : sV2);
+      // P(last, 1st half) meets no barrier before its use: the check here.
+      if constexpr (SM) {
+        if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p0, s_cur, c1, c0);
+        tmax = 0;
+      }
+      accumulate_pv<D>(oacc, p0, vL, 0, lane);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        p1[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SM>(s_nxt[e >> 4][e & 15], c1, c0, tmax);
+      interleave_mfma_valu<2 * C::NB * 2, 10>();
+      if constexpr (SM) {
+        if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p1, s_nxt, c1, c0);
+      }
+      accumulate_pv<D>(oacc, p1, vL, 1, lane);
+      dma_wait();  // the last body's DMA (all zeros) must not outlive the kernel
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // Bodies for tiles 0 .. nkt-2: whole rounds of three (slots 0, 1, 2), then
-    // the one or two left over. The compiler keeps the three-body loop as free
-    // of spills as the earlier form (a loop entered or left in the middle of a
-    // round spilled up to 388 registers); the leftover bodies and the epilogue
-    // sit after it.
-    const int nb = nkt - 1, nb3 = nb / 3 * 3;
-    for (int t = 0; t < nb3; t += 3) {
-      body(I0{}, I2{}, I1{}, t);
-      body(I1{}, I0{}, I2{}, t + 1);
-      body(I2{}, I1{}, I0{}, t + 2);
-    }
-    if (nb3 < nb) body(I0{}, I2{}, I1{}, nb3);
-    if (nb3 + 1 < nb) body(I1{}, I0{}, I2{}, nb3 + 1);
-    // Epilogue, the last tile (slot nb mod 3): P(1st half) V beside
-    // P(2nd half) = sigma(S), then P(2nd half) V.
-    const int last = nb - nb3;
-    const __bf16* vL = last == 0 ? sV0 : (last == 1 ? sV1 : sV2);
-    // P(last, 1st half) meets no barrier before its use: the check here.
     if constexpr (SMALL) {
-      if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p0, s_cur, c1, c0);
-      tmax = 0;
+      if (small_wg) run(std::true_type{});
+      else run(std::false_type{});
+    } else {
+      run(std::false_type{});
     }
-    accumulate_pv<D>(oacc, p0, vL, 0, lane);
-#pragma unroll
-    for (int e = 0; e < 32; ++e)
-      p1[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)sigmoid_pass<SMALL>(s_nxt[e >> 4][e & 15], c1, c0, tmax);
-    interleave_mfma_valu<2 * C::NB * 2, 10>();
-    if constexpr (SMALL) {
-      if (small_sigma_out_of_range(tmax)) sigmoid_exact_block(p1, s_nxt, c1, c0);
-    }
-    accumulate_pv<D>(oacc, p1, vL, 1, lane);
-    dma_wait();  // the last body's DMA (all zeros) must not outlive the kernel
   }
 
   // Epilogue. Register r of oacc[qb][db] holds query row 64w + 32qb + acc_row(r, half), column 32db + l%32.

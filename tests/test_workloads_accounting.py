@@ -74,6 +74,9 @@ def test_profile_kernel_names():
 
     cases = {
         "void sigattn::fwd_bf16_kernel<128>(...)": "fwd",
+        "void sigattn::fwd_bf16_kernel<128, true>(...)": "fwd",
+        "void sigattn::fwd_bf16_kernel<64, false>(...)": "fwd",
+        "_ZN7sigattn15fwd_bf16_kernelILi128ELb1EEEvPKDF16bS2_S2_PDF16bNS_9SeqLayoutEiiffPi": "fwd",
         "void sigattn::dkdv_bf16_kernel<128, 1, 0>(...)": "dk",
         "void sigattn::dkdv_bf16_kernel<128, 2, 1>(...)": "sm_dv",
         "void sigattn::dkdv_bf16_kernel<64, 0, 0>(...)": "dkdv",
