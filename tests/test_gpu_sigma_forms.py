@@ -5,14 +5,18 @@ sigma(S) = t - t^2, t = e^S (one exponential per score; relative error below
 2^-10 while t <= 2^-5, that is S <= -3.47), and keeps the largest t of the
 block. If some score of the block lies outside that range, the wave
 recomputes the whole block with the exact sigma = 1 / (1 + e^-S) before the
-weights are used. A launch whose bias is above -4.16 (where a zero-filled
-padded key alone would leave the range) uses the exact form throughout.
+weights are used. A workgroup whose waves find a score above the range in
+their first block of key tile 0 runs the exact form throughout, and so does
+a launch whose bias is above -4.16 (where a zero-filled padded key alone
+would leave the range).
 
 * Every score in range (small-norm inputs, b = -ln L): the one-exponential
   result is within the bf16 tolerance of the exact oracle.
-* One planted score far above 0 in the last, the first or a middle key tile
-  of a sample: the form t - t^2 would make that weight a large negative
-  number, so the output matches the oracle only if that block was recomputed.
+* One planted score far above 0 in the last or a middle key tile of a sample
+  (a block recomputed inside the key loop), or in the first block of tile 0
+  (the workgroup's vote): the form t - t^2 would make that weight a large
+  negative number, so the output matches the oracle only if the exact form
+  produced it.
 * A bias that rules the one-exponential form out from the start.
 """
 
