@@ -120,6 +120,10 @@ typedef enum {
  *                  query tile from sigattn_tile_config. Entry (z, h, m) receives
  *                  the number of key tiles that query tile m computed. It is 0
  *                  when the tile lies wholly in padding and was skipped.
+ * In bf16, sigma of a block of scores that all lie at or below -3.47 is taken
+ * as t - t^2 with t = e^S (relative error below 2^-10 before P's rounding to
+ * bf16); every other block gets the exact 1 / (1 + e^-S). The result does not
+ * depend on the padding, and is deterministic run to run.
  */
 int sigattn_fwd(const void* q, const void* k, const void* v, void* o,
                 const int32_t* seqlens_q, const int32_t* seqlens_k,
