@@ -73,15 +73,19 @@ __device__ __forceinline__ bool small_sigma_out_of_range(uint32_t tmax) {
   return __builtin_amdgcn_ballot_w64(tmax > kSmallSigmaMaxBits) != 0;
 }
 
-// A launch uses sigmoid_dot_small when c0 = -b log2(e) of its samples is at
-// least this: then a score of 0 (as a zero-filled padded key row gets) has
+// A launch with one bias may use sigmoid_dot_small when c0 = -b log2(e) is
+// at least this: then a score of 0 (as a zero-filled padded key row gets) has
 // t = 2^-c0 <= 2^-6, inside the range, and typical scores are far inside it.
-// For a per-sample bias b_z = bias - ln n_k[z] the test takes n_k = L / 2.
-// Below it nearly every block would need the recomputation.
+// Below it nearly every block would need the recomputation. With a
+// per-sample bias b_z = bias - ln n_k[z] the launch may always use it: the
+// kernel's own test on each workgroup's first block of scores (which a
+// sample whose zero-filled keys score above the range fails) picks the exact
+// form where it does not pay. Neither choice depends on L, so results do not
+// change with the amount of padding.
 constexpr float kSmallSigmaMinC0 = 6.0f;
 
-__host__ __device__ inline bool use_small_sigma(float c0, int L, int bias_per_sample) {
-  return (bias_per_sample ? c0 + __builtin_log2f((float)(L > 2 ? L : 2)) - 1.0f : c0) >= kSmallSigmaMinC0;
+__host__ __device__ inline bool use_small_sigma(float c0, int bias_per_sample) {
+  return bias_per_sample || c0 >= kSmallSigmaMinC0;
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

@@ -493,7 +493,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            float c1, float c0, int32_t* tc, hipStream_t st) {
   using C = FwdCfg<D>;
   const long long blocks = (long long)Z * H * ((sl.L + C::BQ - 1) / C::BQ);
-  if (use_small_sigma(c0, sl.L, sl.bias_per_sample))
+  if (use_small_sigma(c0, sl.bias_per_sample))
     hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, sl, Z, H, c1, c0, tc);
   else

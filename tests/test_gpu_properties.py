@@ -77,15 +77,30 @@ def test_padding_contents_never_matter(fill):
         assert torch.equal(a, b), "a gradient changed with the padding contents"
 
 
-def test_growing_L_is_bitwise_invariant():
+@pytest.mark.parametrize("bias_mode", ["constant", "neg_log_nk"])
+@pytest.mark.parametrize("qk_scale", [1.0, 0.5])
+def test_growing_L_is_bitwise_invariant(bias_mode, qk_scale):
+    """Valid outputs do not change when L grows. At score scale 0.5 the
+    forward's workgroups take the one-transcendental sigma, at 1 most of them
+    the exact one (their first block has scores above its range)."""
+    import padding_aware_sigmoid_amd as sa
+
     Z, L, H, D = 2, 256, 2, 64
     n = np.array([256, 100])
-    note("growing L")
-    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=6)
-    alpha, bias = 0.125, -math.log(256)
-    a = _fwd_bwd(*device_inputs(q, k, v, do, n, n), alpha, bias)
+    note(f"growing L {bias_mode} scale={qk_scale}")
+    q, k, v, do = workloads.make_tensors(Z, L, H, D, "bf16", seed=6, qk_scale=qk_scale)
+    alpha, bias = 0.125, (-math.log(256) if bias_mode == "constant" else 0.0)
+
+    def run(q, k, v, do):
+        dq_, dk_, dv_, ddo, dn, _ = device_inputs(q, k, v, do, n, n)
+        o = sa.sigattn_fwd(dq_, dk_, dv_, dn, dn, alpha, bias, bias_mode=bias_mode)
+        g = sa.sigattn_bwd(dq_, dk_, dv_, ddo, dn, dn, alpha, bias, bias_mode=bias_mode)
+        torch.cuda.synchronize()
+        return o, g
+
+    a = run(q, k, v, do)
     grow = lambda t: torch.cat([t, torch.randn(Z, 70, H, D).to(t.dtype)], dim=1)  # noqa: E731
-    b = _fwd_bwd(*device_inputs(grow(q), grow(k), grow(v), grow(do), n, n), alpha, bias)
+    b = run(grow(q), grow(k), grow(v), grow(do))
     assert torch.equal(a[0], b[0][:, :L]) and torch.all(b[0][:, L:] == 0)
     for x, y in zip(a[1], b[1]):
         assert torch.equal(x, y[:, :L]) and torch.all(y[:, L:] == 0)
