@@ -291,9 +291,9 @@ __global__ __launch_bounds__(256, kWavesPerSimd<D>) void fwd_bf16_kernel(const _
       dma_tile<D, C::BK, 256>(sv, Vb + off, row_bytes, nk - k0, tid);
     };
     // A launch allowed the one-transcendental form (SMALL) takes it in a
-    // workgroup only if every wave's first 32 x 32 block of scores lies well
-    // inside the form's range (t <= 2^-6), tested on K tile 0 before the key
-    // loop. Inputs whose scores leave the range (large norms) show it at
+    // workgroup only if the scores of every wave's 64 queries against keys
+    // 0 .. 31 lie well inside the form's range (t <= 2^-6), tested on K tile
+    // 0 before the key loop. Inputs whose scores leave the range (large norms) show it at
     // once, and the workgroup then runs the exact form throughout instead of
     // computing most blocks twice. Either way each block is checked before
     // use. The decision is the workgroup's (a vote in LDS), so all waves run

@@ -100,3 +100,29 @@ def test_bias_outside_the_range_runs_the_exact_sigma(D):
     alpha, bias = 1 / math.sqrt(D), -2.0
     q, k, v, _ = _inputs(Z, L, H, D, seed=42, qk_scale=1.0)
     _forward_parity(q, k, v, n, alpha, bias, f"bias -2 D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_one_exponential_form_every_tile_count(D):
+    """Samples of 1 to 5 key tiles, full and partial, with scores inside the
+    one-exponential range (so every workgroup takes that form): the prologue,
+    the leftover iterations after the loop in rounds of three, and the last
+    tile's epilogue each check their blocks. Tile counters equal the plan."""
+    import padding_aware_sigmoid_amd as sa
+
+    lengths = [1, 40, 64, 65, 100, 128, 129, 192, 200, 256, 300]
+    Z, L, H = len(lengths), 320, 1
+    n = np.array(lengths)
+    alpha, bias = 1 / math.sqrt(D), -math.log(L)
+    q, k, v, _ = _inputs(Z, L, H, D, seed=43, qk_scale=0.4)
+    s = np.einsum("zihd,zjhd->zhij", f64(q), f64(k)) * alpha + bias
+    # every workgroup's vote passes (t <= 2^-6, that is S <= -4.16), with room
+    assert float(s.max()) < -4.16 - 0.5
+    _forward_parity(q, k, v, n, alpha, bias, f"every tile count D={D}")
+    dq_, dk_, dv_, _, dn, _ = device_inputs(q, k, v, v, n, n)
+    bq, bk = sa.sigattn_tile_config(sa.KERNEL_FWD, D, dq_.dtype)
+    tc = torch.full((Z * H * (-(-L // bq)),), -7, dtype=torch.int32, device=dq_.device)
+    sa.sigattn_fwd(dq_, dk_, dv_, dn, dn, alpha, bias, tile_counts=tc)
+    torch.cuda.synchronize()
+    by_q, _ = oracle.tile_plan(n, n, L, bq, bk)
+    assert np.array_equal(tc.cpu().numpy().reshape(Z, H, -1)[:, 0, :], by_q)
