@@ -121,7 +121,7 @@ typedef enum {
  *                  the number of key tiles that query tile m computed. It is 0
  *                  when the tile lies wholly in padding and was skipped.
  * In bf16, sigma of a block of scores that all lie at or below -3.47 is taken
- * as t - t^2 with t = e^S (relative error below 2^-10 before P's rounding to
+ * as t - t^2 with t = e^S (relative error t^2 <= 2^-10 before P's rounding to
  * bf16); every other block gets the exact 1 / (1 + e^-S). The result does not
  * depend on the padding, and is deterministic run to run.
  */

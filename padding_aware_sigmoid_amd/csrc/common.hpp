@@ -46,8 +46,9 @@ __device__ __forceinline__ float sigmoid_dot(float s, float c1, float c0) {
 
 // sigma with one transcendental, for scores far below 0. With t = e^S =
 // 2^(-c1*s - c0), sigma(S) = t / (1 + t) = t - t^2 + t^3 / (1 + t), so t - t^2
-// (one FMA) has relative error t^2 / (1 + t) < t^2: below 2^-10, a quarter of
-// P's bf16 rounding step, while t <= 2^-5 (S <= -3.47). The bias b = -ln n of
+// (one FMA) is short by t^3 / (1 + t), a relative error of exactly t^2: at
+// most 2^-10, a quarter of P's bf16 rounding step, while t <= 2^-5
+// (S <= -3.47). The bias b = -ln n of
 // the method puts nearly every score there (S ~ b + N(0, 1) for unit-variance
 // inputs, b = -9 at n = 8192). The caller keeps the bit pattern of the
 // largest t in tmax (t >= 0, so unsigned order is float order, and a NaN t

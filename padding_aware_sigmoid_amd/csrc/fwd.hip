@@ -24,7 +24,7 @@
 //  - V reaches the MFMA through ds_read_b64_tr_b16.
 //  - sigma takes one v_exp_f32 and one FMA per score, t - t^2 with t = e^S,
 //    on every 32 x 32 block of weights whose scores all lie at or below -3.47
-//    (relative error under 2^-10; the bias b = -ln n puts nearly all scores
+//    (relative error t^2, at most 2^-10; the bias b = -ln n puts nearly all scores
 //    there), and the exact 1 / (1 + e^-S) (v_exp_f32, v_rcp_f32) on the
 //    others: a ballot after each block tells the wave to recompute it. A
 //    workgroup whose first block of scores already leaves that range (large

@@ -1,8 +1,8 @@
 """The forward's two forms of sigma, against the oracle.
 
 The bf16 forward computes each 32 x 32 block of weights of a wave with
-sigma(S) = t - t^2, t = e^S (one exponential per score; relative error below
-2^-10 while t <= 2^-5, that is S <= -3.47), and keeps the largest t of the
+sigma(S) = t - t^2, t = e^S (one exponential per score; relative error t^2, at
+most 2^-10 while t <= 2^-5, that is S <= -3.47), and keeps the largest t of the
 block. If some score of the block lies outside that range, the wave
 recomputes the whole block with the exact sigma = 1 / (1 + e^-S) before the
 weights are used. A workgroup whose waves find a score above the range in
