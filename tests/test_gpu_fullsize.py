@@ -19,7 +19,13 @@ Two bounds hold every sampled output:
   is rounded to bf16 once (at most u |ref|). The bound is
       1.01 u |ref| + 6 (u / sqrt 3) sqrt(sum_j w_j^2 x_j^2)
                    + 6 * 2^-24 sqrt(n) sum_j |w_j x_j|
-  per element, with w, x the weight and operand of the contraction. Six
+  per element, with w, x the weight and operand of the contraction. The
+  bf16 forward takes P = t - t^2 (t = e^S) on blocks whose every t is at
+  most 2^-5; that form undershoots sigma by at most t^2 of it, one-sided, so
+  O's bound adds sum_j t_j^2 |P_j V_j| over the keys with t_j in that range
+  (to 2^-18 above it, the kernel's own error in t). At these workloads'
+  biases t is below 1e-3 for nearly every key and the term is negligible;
+  it keeps the bound true wherever larger scores take that form. Six
   standard deviations over the few thousand sampled elements of a run leave
   a chance of a false failure far below 1e-6. For O at 16K keys its largest
   value is about 1e-2 of max|ref|, and every element is held to its own
@@ -43,13 +49,30 @@ U_FP32 = 2.0 ** -24
 N_SIGMA = 6.0
 
 
-def _derived_bound(ref, w, x, scale=1.0):
-    """Elementwise bound on |got - ref| for ref = scale * w @ x (w: [rows, n], x: [n, D])."""
+def _derived_bound(ref, w, x, scale=1.0, w_rel=None):
+    """Elementwise bound on |got - ref| for ref = scale * w @ x (w: [rows, n], x: [n, D]).
+
+    w_rel, if given, is a one-sided relative deviation of each weight that the
+    kernel may carry besides its rounding; it adds scale * (w_rel |w|) @ |x|."""
     n = w.shape[1]
     stat = np.sqrt((w * w) @ (x * x))
     absum = np.abs(w) @ np.abs(x)
-    return (1.01 * U_BF16 * np.abs(ref) + scale * N_SIGMA * (U_BF16 / np.sqrt(3.0)) * stat
-            + scale * N_SIGMA * U_FP32 * np.sqrt(max(n, 1)) * absum)
+    bound = (1.01 * U_BF16 * np.abs(ref) + scale * N_SIGMA * (U_BF16 / np.sqrt(3.0)) * stat
+             + scale * N_SIGMA * U_FP32 * np.sqrt(max(n, 1)) * absum)
+    if w_rel is not None:
+        bound = bound + scale * ((w_rel * np.abs(w)) @ np.abs(x))
+    return bound
+
+
+T_SMALL = 2.0 ** -5  # largest t = e^S of a block the forward computes as t - t^2
+
+
+def _small_sigma_rel(S):
+    """Relative shortfall t^2 of the weight t - t^2 against sigma(S), for every
+    score the one-exponential form may take (t up to 2^-5, with a margin of
+    2^-18 for the kernel's own t); 0 where the exact form is certain."""
+    t = np.exp(np.minimum(S, 0.0))
+    return np.where(t <= T_SMALL * (1.0 + 2.0 ** -18), t * t, 0.0)
 
 
 def _sample_rows(n, L, rng):
@@ -105,7 +128,7 @@ def _run_full(name, qk_scale=None, heads_per_sample=2, seed=0):
             if lq.any():
                 *_, im = oracle.head_backward(Q[z, qrows[lq], h], K[z, :b, h], V[z, :b, h], DO[z, qrows[lq], h],
                                               w.alpha, bz, return_intermediates=True)
-                bo[lq] = _derived_bound(o_ref[lq], im["P"], V[z, :b, h])
+                bo[lq] = _derived_bound(o_ref[lq], im["P"], V[z, :b, h], w_rel=_small_sigma_rel(im["S"]))
                 bdq[lq] = _derived_bound(dq_ref[lq], im["dS"], K[z, :b, h], w.alpha)
             if lk.any():
                 *_, im = oracle.head_backward(Q[z, :a, h], K[z, krows[lk], h], V[z, krows[lk], h], DO[z, :a, h],
